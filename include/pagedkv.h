@@ -1,0 +1,207 @@
+/*
+ * pagedkv.h — paged KV-cache decode attention and KV append for AMD Instinct
+ * MI355X (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * The operations follow two web pages:
+ *   [A] "PagedAttention Paper Breakdown: Virtual Memory Allocation for LLM KV
+ *       Cache Serving", section 2, "Address Translation Formula": token i of a
+ *       sequence lives in logical block b = floor(i / B) at offset o = i mod B,
+ *       and its physical location is T[b] * B + o, T being the sequence's
+ *       block table.
+ *   [B] "PagedAttention and vLLM Architecture: Virtual Memory for LLM Serving":
+ *       section 1 (a physical page holds the Key and Value of B tokens; the
+ *       block table is kept by the serving engine), "Why Internal Fragmentation
+ *       is Bounded" (a block is added only when a new token overflows the last
+ *       one) and section 2, "PagedAttention Attention CUDA Kernel Mechanics"
+ *       (the decode kernel takes the query and the block table, walks the
+ *       physical blocks, dots the query with every key, and finishes with an
+ *       online softmax fused with the product by the Value blocks).
+ *
+ * Common conventions
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *     where stated.  Buffers are dense, row-major, 16-byte aligned.
+ *   - Cache layout: k_cache and v_cache are [num_blocks, B, kv_heads, head_dim]
+ *     of `dtype`.  Slot s = T[b] * B + o names row s of the pool viewed as
+ *     [num_blocks * B, kv_heads, head_dim]; K and V share tables and slots.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The library never allocates, frees or synchronises, and keeps
+ *     no state between calls: it is safe to call from several host threads.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     negative status means nothing was enqueued.  PKV_ERR_HIP means a launch
+ *     failed (hipGetLastError after the launch).
+ *   - Device-side contract (not checked, for cost, except where stated):
+ *     table entries read by a call lie in [0, num_blocks); append slots are
+ *     distinct; no slot is written while its block is shared by several
+ *     sequences (copy-on-write must already have given the writer a private
+ *     block).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  PKV_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or
+                               inconsistent with another                          */
+  PKV_ERR_DTYPE = -3,       /* dtype is not PKV_DTYPE_F32 or PKV_DTYPE_BF16       */
+  PKV_ERR_UNSUPPORTED = -4, /* valid but outside the compiled set (head_dim,
+                               block size, group size, partition size)            */
+  PKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
+  PKV_ERR_HIP = -6          /* a kernel launch failed                             */
+};
+
+enum pkv_dtype {
+  PKV_DTYPE_F32 = 0,  /* IEEE binary32                                          */
+  PKV_DTYPE_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32             */
+};
+
+/*
+ * paged_kv_slot_mapping — [A] applied to the position each sequence writes
+ * next ([B], "Why Internal Fragmentation is Bounded": a sequence holding L
+ * tokens writes its next token at logical position L, in the block the engine
+ * appended to its table when L crossed a block boundary).
+ *
+ *   slot_mapping [num_seqs]  int32, written: T[s][p / B] * B + p % B for
+ *                            p = positions[s]; -1 when p < 0 or
+ *                            p >= max_blocks_per_seq * B.
+ *   block_tables [num_seqs, max_blocks_per_seq] int32, read at column p / B only.
+ *   positions    [num_seqs]  int32.
+ * Requires num_blocks * block_size <= INT32_MAX (slots are int32).
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE; num_seqs == 0 enqueues nothing.
+ */
+PKV_API int paged_kv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, const int32_t* positions,
+                          int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                          int32_t num_blocks, void* stream);
+
+/*
+ * paged_kv_append — the slot write of [B] ("Why Internal Fragmentation is
+ * Bounded"; section 1: K and V of a token share its slot).  For every token t
+ * with 0 <= slot_mapping[t] < num_blocks * block_size, copies the row
+ * k_new[t] ([kv_heads, head_dim]) to k_cache slot slot_mapping[t] and v_new[t]
+ * to v_cache at the same slot, bit for bit.  Tokens with any other slot are
+ * skipped (so a stray slot can never write outside the pool).
+ *
+ *   k_cache, v_cache [num_blocks, block_size, kv_heads, head_dim] dtype, in/out.
+ *   k_new, v_new     [num_tokens, kv_heads, head_dim] dtype, read.
+ *   slot_mapping     [num_tokens] int32, read.
+ * kv_heads * head_dim * element size must be a multiple of 16 bytes.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE; num_tokens == 0 enqueues
+ * nothing.
+ */
+PKV_API int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                    int32_t block_size, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                    void* stream);
+
+/*
+ * paged_attn_decode — one decode step of paged attention, [B] section 2 with
+ * the table walk of [A].  For every sequence s (L = context_lens[s]) and query
+ * head h (kv head g = h / (q_heads / kv_heads)):
+ *
+ *   x_i = scale * <q[s,h,:], K_i[g,:]>   for logical positions i = 0 .. L-1,
+ *   out[s,h,:] = sum_i softmax(x)_i * V_i[g,:]
+ *
+ * where K_i / V_i are read from slot T[s][i / B] * B + i % B.  Scores, the
+ * online softmax and the V accumulation are fused in one pass over each
+ * sequence's physical blocks, all in fp32; long contexts are split into
+ * partitions of `partition_size` tokens whose partial results are merged by a
+ * second kernel (log-sum-exp rescaling).  The result does not depend on which
+ * physical blocks hold the tokens: reductions follow logical positions only,
+ * so permuting the pool, or sharing blocks between sequences, gives bitwise
+ * identical outputs, and repeated calls are bitwise deterministic.
+ *
+ *   out          [num_seqs, q_heads, head_dim] fp32, written (every element).
+ *   q            [num_seqs, q_heads, head_dim] dtype.
+ *   k_cache, v_cache [num_blocks, block_size, kv_heads, head_dim] dtype.
+ *   block_tables [num_seqs, max_blocks_per_seq] int32; only entries
+ *                b < ceil(L / B) are read.
+ *   context_lens [num_seqs] int32.  L = 0 gives zeros.  A sequence with
+ *                L < 0 or L > max_context_len gets NaN rows (it cannot be
+ *                covered by the launch); a table entry outside
+ *                [0, num_blocks) is not dereferenced and also gives NaN rows.
+ *   max_context_len  host-side upper bound of context_lens; sizes the grid.
+ *                    Must be <= max_blocks_per_seq * block_size.
+ *   scale        multiplies the dot products (e.g. 1/sqrt(head_dim)).
+ *   partition_size   tokens per partition: 0 = choose automatically, else a
+ *                    multiple of 16 in [16, 8192].
+ *   workspace    device scratch of at least
+ *                paged_attn_decode_workspace_size(...) bytes, same arguments;
+ *                may be NULL when that size is 0.  Overwritten.
+ *
+ * Supported: dtype F32 or BF16 (q, K, V share it); head_dim 64 or 128;
+ * block_size 16 or 32; q_heads % kv_heads == 0 with group size 1, 2, 4, 8 or 16.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED,
+ * PKV_ERR_WORKSPACE, PKV_ERR_HIP.  num_seqs == 0 enqueues nothing.
+ */
+PKV_API int paged_attn_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                      float scale, int32_t dtype, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of paged_attn_decode, for callers that time or schedule them
+ * apart.  Same arguments and checks.  Stage 1 runs the fused score / online
+ * softmax / V pass per (sequence, kv head, partition); when the resolved plan
+ * has a single partition it writes `out` directly and stage 2 enqueues
+ * nothing.  Otherwise stage 1 writes per-partition (max, sum, accumulator)
+ * triples to the workspace and stage 2 merges them into `out`.  Stage 2 must
+ * follow stage 1 on the same stream with the same arguments.
+ */
+PKV_API int paged_attn_decode_partitions(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                 int32_t max_context_len, float scale, int32_t dtype,
+                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+PKV_API int paged_attn_decode_reduce(float* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                             float scale, int32_t dtype, int32_t partition_size, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode_plan — the partition size and partition count a call with
+ * these arguments uses (partition_size 0 = the automatic choice).  Host only;
+ * writes *resolved_partition_size and *num_partitions (either may be NULL).
+ * Returns PKV_OK or the error the decode call would return for these sizes.
+ */
+PKV_API int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t max_context_len, int32_t dtype,
+                           int32_t partition_size, int32_t* resolved_partition_size,
+                           int32_t* num_partitions);
+
+/*
+ * paged_attn_decode_workspace_size — bytes of workspace paged_attn_decode needs
+ * for these arguments: 0 when the plan has a single partition, else
+ * num_seqs * q_heads * num_partitions * (head_dim + 2) * 4 bytes (rounded up
+ * to 256).  Host only.  Returns 0 for arguments the decode call would reject.
+ */
+PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                        int32_t dtype, int32_t partition_size);
+
+/* paged_status_str — a static, human-readable name for a status code. */
+PKV_API const char* paged_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

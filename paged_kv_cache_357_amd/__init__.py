@@ -1,0 +1,20 @@
+"""Paged KV-cache decode attention and KV append for MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+libpagedkv.so (include/pagedkv.h); this package is its Python binding.
+"""
+from ._lib import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F32,
+    LIB_PATH,
+    SIGNATURES,
+    DecodeCall,
+    PagedKVError,
+    append,
+    decode,
+    load_library,
+    plan,
+    slot_mapping,
+    status_str,
+    workspace_size,
+)

@@ -1,0 +1,77 @@
+// Slot mapping and KV append for gfx950.
+//
+// Slot of logical position p: T[p / B] * B + p % B ("PagedAttention Paper
+// Breakdown", section 2, Address Translation Formula).  A sequence holding L
+// tokens writes its next token at position L, into the block the engine added
+// to its table when L reached a block boundary ("PagedAttention and vLLM
+// Architecture", Why Internal Fragmentation is Bounded).  K and V of a token
+// share the slot (same page, section 1).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(int32_t* __restrict__ slots,
+                                                           const int32_t* __restrict__ tables,
+                                                           const int32_t* __restrict__ positions, int S, int MB,
+                                                           int B) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= S) return;
+  const int p = positions[s];
+  int slot = -1;
+  if (p >= 0 && (long long)p < (long long)MB * B) {
+    const int b = p / B;
+    slot = tables[(size_t)s * MB + b] * B + (p - b * B);
+  }
+  slots[s] = slot;
+}
+
+// One thread per 16-byte column of a row; consecutive threads cover
+// consecutive columns of one token's row, so both the read of k_new / v_new
+// and the write into the slot are fully coalesced.
+__global__ __launch_bounds__(256) void append_kernel(char* __restrict__ kc, char* __restrict__ vc,
+                                                     const char* __restrict__ kn, const char* __restrict__ vn,
+                                                     const int32_t* __restrict__ slots, int N, long long num_slots,
+                                                     int cols16) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long t = gid / cols16;
+  const int c = (int)(gid - t * cols16);
+  if (t >= N) return;
+  const int slot = slots[t];
+  if (slot < 0 || (long long)slot >= num_slots) return;
+  const size_t row = (size_t)cols16 * 16;
+  const uint4 kv = reinterpret_cast<const uint4*>(kn + (size_t)t * row)[c];
+  const uint4 vv = reinterpret_cast<const uint4*>(vn + (size_t)t * row)[c];
+  reinterpret_cast<uint4*>(kc + (size_t)slot * row)[c] = kv;
+  reinterpret_cast<uint4*>(vc + (size_t)slot * row)[c] = vv;
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(int32_t* slots, const int32_t* tables, const int32_t* positions, int S, int MB,
+                               int B, hipStream_t stream) {
+  if (S == 0) return hipSuccess;
+  const int threads = 256;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((S + threads - 1) / threads), dim3(threads), 0, stream, slots,
+                     tables, positions, S, MB, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* slots,
+                         int N, long long num_slots, int row_bytes, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int cols16 = row_bytes / 16;
+  const long long total = (long long)N * cols16;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, static_cast<char*>(k_cache),
+                     static_cast<char*>(v_cache), static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+                     slots, N, num_slots, cols16);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,335 @@
+"""GPU parity of the HIP path against the fp64 oracle, and GPU properties.
+
+Every call goes through the C ABI (libpagedkv.so) via the ctypes binding.
+Tolerances are the stated ones: max |gpu - oracle| <= 1e-4 for fp32 KV and
+5e-4 for bf16 KV; slot mapping and append are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.paged_attention as pa
+from workloads import make_config, make_small, make_workload, permute_pool, poison_unused, raw_numpy
+from gpu_common import TOL, assert_parity, gpu_decode, oracle_out, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_357_amd as pk
+    pk.load_library()
+    return pk
+
+
+_FULL = {}
+
+
+def full(k):
+    if k not in _FULL:
+        _FULL.clear()  # keep one full-size workload resident at a time
+        say(f"generating full config {k}")
+        w = make_config(k)
+        _FULL[k] = (w, to_gpu(w))
+    return _FULL[k]
+
+
+# ----------------------------------------------------------- small parity
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("P", [0, 16, 32, 64, 256, 512, 8192])
+def test_small_decode_matches_oracle(pk, k, P):
+    w = make_small(k)
+    say(f"small config {k} partition {P} S={w.num_seqs} max L={w.max_context_len}")
+    d = to_gpu(w)
+    out = gpu_decode(pk, w, d, partition_size=P)
+    ref = oracle_out(w)
+    assert_parity(out, ref, w, what=f"P={P}")
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_small_slots_append_then_decode(pk, k):
+    w = make_small(k)
+    d = to_gpu(w)
+    B = w.block_size
+    slots = pk.slot_mapping(d.tables, d.lens, w.num_blocks, B).cpu().numpy()
+    ref_slots = pa.oracle_slot_mapping(w.block_tables, w.context_lens, B)
+    assert np.array_equal(slots.astype(np.int64), ref_slots)
+    pk.append(d.k, d.v, d.kn, d.vn, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    k2, v2 = pa.oracle_append(raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables, w.context_lens,
+                              raw_numpy(w.k_new), raw_numpy(w.v_new), B)
+    gk, gv = raw_numpy(d.k.cpu()), raw_numpy(d.v.cpu())
+    assert np.array_equal(gk.view(np.uint8), k2.view(np.uint8))
+    assert np.array_equal(gv.view(np.uint8), v2.view(np.uint8))
+    lens1 = w.context_lens + 1
+    out = gpu_decode(pk, w, d, lens=lens1)
+    ref = oracle_out(w, lens=lens1, k_cache=k2, v_cache=v2)
+    assert_parity(out, ref, w, what="decode(L+1) after append")
+
+
+def test_stages_equal_whole_call(pk):
+    w = make_small(5)
+    d = to_gpu(w)
+    call = pk.DecodeCall(d.q, d.k, d.v, d.tables, d.lens, w.scale, w.max_context_len, 256)
+    a = call.run().clone()
+    call.out.zero_()
+    call.partitions()
+    call.reduce()
+    torch.cuda.synchronize()
+    assert call.plan[1] > 1
+    assert torch.equal(a, call.out)
+
+
+def test_wide_group_and_fp32_d128(pk):
+    # the largest compiled group (16) and the fp32 / head_dim 128 variant
+    for dtype, D, B in (("f32", 128, 16), ("bf16", 128, 32), ("f32", 64, 32), ("bf16", 64, 16)):
+        w = make_workload(f"g16-{dtype}-{D}-{B}", [1, 17, 300, 1000], 32, 2, D, B, dtype, 99)
+        d = to_gpu(w)
+        for P in (0, 64):
+            assert_parity(gpu_decode(pk, w, d, partition_size=P), oracle_out(w), w, what=f"G=16 P={P}")
+
+
+# ------------------------------------------------------------ full sizes
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_full_config(pk, k):
+    """Decode at the benchmark's launch configuration, determinism, then the
+    slot write and decode(L+1), on the full-size workload."""
+    w, d = full(k)
+    dt = pk.DTYPE_BF16 if w.dtype == "bf16" else pk.DTYPE_F32
+    say(f"full config {k}: S={w.num_seqs} sum L={int(w.context_lens.sum())} "
+        f"plan={pk.plan(w.num_seqs, w.q_heads, w.kv_heads, w.head_dim, w.block_size, w.max_context_len, dt)}")
+    out = gpu_decode(pk, w, d)
+    if k <= 3:
+        seqs = None
+    elif k == 4:
+        seqs = [0, 1, 2, 3, 17, 130, 257, 511]
+    else:
+        seqs = [0, 5]
+    ref = oracle_out(w, seqs=seqs)
+    assert_parity(out, ref, w, seqs=seqs, what="decode(L)")
+    again = gpu_decode(pk, w, d)
+    assert np.array_equal(out.view(np.uint32), again.view(np.uint32)), "not deterministic"
+
+    B = w.block_size
+    slots_t = pk.slot_mapping(d.tables, d.lens, w.num_blocks, B)
+    slots = slots_t.cpu().numpy().astype(np.int64)
+    assert np.array_equal(slots, pa.oracle_slot_mapping(w.block_tables, w.context_lens, B))
+    ib = torch.int16 if w.dtype == "bf16" else torch.int32
+    before_k = d.k.clone()
+    before_v = d.v.clone()
+    pk.append(d.k, d.v, d.kn, d.vn, slots_t)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(slots).cuda()
+    mask = torch.ones(w.num_blocks * B, dtype=torch.bool, device="cuda")
+    mask[idx] = False
+    for pool, before, new in ((d.k, before_k, d.kn), (d.v, before_v, d.vn)):
+        flat = pool.view(w.num_blocks * B, -1).view(ib)
+        assert torch.equal(flat.index_select(0, idx), new.reshape(len(slots), -1).view(ib))
+        assert torch.equal(flat[mask], before.view(w.num_blocks * B, -1).view(ib)[mask])
+    del before_k, before_v
+    if k == 4:
+        shared = torch.from_numpy(np.unique(w.block_tables[:, :w.meta["prompt_blocks"]]).astype(np.int64))
+        assert torch.equal(d.k.index_select(0, shared.cuda()).cpu(), w.k_cache.index_select(0, shared))
+    lens1 = w.context_lens + 1
+    seqs1 = [0, 1] if k >= 4 else list(range(min(8, w.num_seqs)))
+    out1 = gpu_decode(pk, w, d, lens=lens1)
+    k2, v2 = raw_numpy(d.k.cpu()), raw_numpy(d.v.cpu())
+    ref1 = oracle_out(w, lens=lens1, seqs=seqs1, k_cache=k2, v_cache=v2)
+    assert_parity(out1, ref1, w, seqs=seqs1, what="decode(L+1) after append")
+    _FULL.pop(k, None)  # the pools now differ from the generator's
+
+
+def test_full_long_context_partition_sizes(pk):
+    w, d = full(5)
+    ref = oracle_out(w, seqs=[3])
+    for P in (256, 512, 1024, 8192):
+        out = gpu_decode(pk, w, d, partition_size=P)
+        assert_parity(out, ref, w, seqs=[3], what=f"P={P}")
+
+
+def test_full_permutation_invariance_bitwise(pk):
+    w, d = full(5)
+    a = gpu_decode(pk, w, d)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(w.num_blocks)).cuda()
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(w.num_blocks, device="cuda")
+    k2 = d.k.index_select(0, inv)
+    v2 = d.v.index_select(0, inv)
+    t2 = perm[d.tables.long()].to(torch.int32).contiguous()
+    lens = d.lens
+    out = pk.decode(d.q, k2, v2, t2, lens, w.scale, w.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.view(np.uint32), out.cpu().numpy().view(np.uint32))
+
+
+# -------------------------------------------------------------- properties
+
+@pytest.mark.parametrize("k", [2, 3, 5])
+def test_permutation_invariance_bitwise(pk, k):
+    w = make_small(k)
+    perm = np.random.default_rng(100 + k).permutation(w.num_blocks)
+    for P in (0, 64):
+        a = gpu_decode(pk, w, to_gpu(w), partition_size=P)
+        b = gpu_decode(pk, w, to_gpu(permute_pool(w, perm)), partition_size=P)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_cow_siblings_bitwise(pk):
+    w = make_small(4)
+    n_prompts, n_sib, _ = w.meta["prompts"]
+    pb = w.meta["prompt_blocks"]
+    tables = w.block_tables.astype(np.int64).copy()
+    extra, nxt = [], w.num_blocks
+    for s in range(w.num_seqs):
+        if s % n_sib:
+            for b in range(pb):
+                extra.append(int(tables[s, b]))
+                tables[s, b] = nxt
+                nxt += 1
+    idx = torch.tensor(extra, dtype=torch.long)
+    w2 = make_small(4)
+    w2.k_cache = torch.cat([w.k_cache, w.k_cache.index_select(0, idx)])
+    w2.v_cache = torch.cat([w.v_cache, w.v_cache.index_select(0, idx)])
+    w2.block_tables = tables.astype(np.int32)
+    w2.num_blocks = nxt
+    a = gpu_decode(pk, w, to_gpu(w))
+    b = gpu_decode(pk, w2, to_gpu(w2))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    w3 = make_small(4, shared_q=True, zero_tails=True)
+    o3 = gpu_decode(pk, w3, to_gpu(w3))
+    for j in range(n_prompts):
+        for s in range(1, n_sib):
+            assert np.array_equal(o3[j * n_sib].view(np.uint32), o3[j * n_sib + s].view(np.uint32))
+    assert_parity(o3, oracle_out(w3), w3, what="cow identical siblings")
+
+
+def _needle_sweep(L, Hq, Hkv, D, B, dtype, seed):
+    """L sequences of length L; sequence s hides its needle at position s."""
+    w = make_workload(f"needle-{L}-{dtype}-G{Hq // Hkv}", [L] * L, Hq, Hkv, D, B, dtype, seed)
+    q = torch.zeros_like(w.q)
+    q[:, :, 0] = 16.0
+    k = torch.zeros_like(w.k_cache)
+    kf = k.view(w.num_blocks * B, Hkv, D)
+    for s in range(L):
+        kf[pa.slot_of(w.block_tables[s], s, B), :, 0] = 16.0
+    w.q, w.k_cache, w.scale = q, k, 1.0
+    return w
+
+
+@pytest.mark.parametrize("case", [(40, 4, 4, 64, 16, "f32"), (300, 2, 2, 128, 16, "bf16"),
+                                  (600, 8, 1, 128, 16, "bf16"), (200, 8, 2, 128, 32, "bf16")])
+def test_needle_every_position_bit_exact(pk, case):
+    L, Hq, Hkv, D, B, dt = case
+    w = _needle_sweep(L, Hq, Hkv, D, B, dt, 7)
+    d = to_gpu(w)
+    vflat = w.v_cache.float().view(w.num_blocks * B, Hkv, D).numpy()
+    G = Hq // Hkv
+    exp = np.empty((L, Hq, D), dtype=np.float32)
+    for s in range(L):
+        row = vflat[pa.slot_of(w.block_tables[s], s, B)]
+        for h in range(Hq):
+            exp[s, h] = row[h // G]
+    for P in (0, 64, 16):
+        out = gpu_decode(pk, w, d, partition_size=P)
+        bad = np.argwhere(out.view(np.uint32) != exp.view(np.uint32))
+        assert bad.size == 0, (P, bad[:5])
+
+
+def test_position_sum_closed_form(pk):
+    for k in (1, 2, 3, 5):
+        w = make_small(k)
+        q, v = (np.zeros_like(raw_numpy(w.q)), np.zeros_like(raw_numpy(w.v_cache)))
+        flat = v.reshape(-1, w.kv_heads, w.head_dim)
+        for s in range(w.num_seqs):
+            for i in range(int(w.context_lens[s])):
+                slot = pa.slot_of(w.block_tables[s], i, w.block_size)
+                a, b = np.float32(i % 256), np.float32(i // 256)
+                if w.dtype == "bf16":
+                    a, b = a.view(np.uint32) >> 16, b.view(np.uint32) >> 16
+                flat[slot, :, 0], flat[slot, :, 1] = a, b
+        d = to_gpu(w)
+        if w.dtype == "bf16":
+            d.q = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+            d.v = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            d.q, d.v = torch.from_numpy(q).cuda(), torch.from_numpy(v).cuda()
+        for P in (0, 16, 256):
+            out = gpu_decode(pk, w, d, partition_size=P)
+            for s in range(w.num_seqs):
+                L = int(w.context_lens[s])
+                full_, rem = divmod(L, 256)
+                mod_sum = full_ * (255 * 256 // 2) + rem * (rem - 1) // 2
+                div_sum = 256 * (full_ * (full_ - 1) // 2) + full_ * rem
+                e0 = np.float32(mod_sum) / np.float32(L)
+                e1 = np.float32(div_sum) / np.float32(L)
+                assert np.all(out[s, :, 0] == e0), (k, P, s, out[s, :, 0], e0)
+                assert np.all(out[s, :, 1] == e1), (k, P, s)
+                assert np.all(out[s, :, 2:] == 0)
+
+
+def test_nan_poison_never_reaches_output(pk):
+    for k in (1, 2, 3, 4, 5):
+        w = make_small(k)
+        clean = gpu_decode(pk, w, to_gpu(w))
+        z = poison_unused(w)
+        kf = z.k_cache.view(z.num_blocks * z.block_size, -1)
+        vf = z.v_cache.view(z.num_blocks * z.block_size, -1)
+        for s in range(z.num_seqs):
+            L = int(z.context_lens[s])
+            end = -(-(L + 1) // z.block_size) * z.block_size
+            for i in range(L, end):  # unwritten tail slots of the owned blocks
+                slot = pa.slot_of(z.block_tables[s], i, z.block_size)
+                kf[slot] = float("nan")
+                vf[slot] = float("nan")
+        for P in (0, 16):
+            a = gpu_decode(pk, w, to_gpu(w), partition_size=P) if P else clean
+            b = gpu_decode(pk, z, to_gpu(z), partition_size=P)
+            assert np.all(np.isfinite(b)), k
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), k
+
+
+def test_degenerate_lengths(pk):
+    w = make_small(2)
+    d = to_gpu(w)
+    maxL = w.max_context_len
+    lens = w.context_lens.copy()
+    lens[0] = 0
+    lens[1] = 1
+    for P in (0, 64):
+        out = gpu_decode(pk, w, d, lens=lens, max_len=maxL, partition_size=P)
+        assert np.all(out[0] == 0)
+        v = w.v_cache.float().numpy()
+        p0 = int(w.block_tables[1, 0])
+        for h in range(w.q_heads):
+            assert np.array_equal(out[1, h], v[p0, 0, h // w.group])
+        ref = oracle_out(w, lens=lens, seqs=range(2, w.num_seqs))
+        assert_parity(out, ref, w, seqs=range(2, w.num_seqs), what=f"L=0/1 mix P={P}")
+    # all sequences empty
+    out = gpu_decode(pk, w, d, lens=np.zeros(w.num_seqs, np.int32), max_len=0)
+    assert np.all(out == 0)
+
+
+def test_invalid_lengths_and_blocks_give_nan_rows(pk):
+    w = make_small(2)
+    d = to_gpu(w)
+    maxL = w.max_context_len
+    lens = w.context_lens.copy()
+    lens[0] = maxL + 1        # beyond the launch's bound
+    lens[1] = -3
+    ref = oracle_out(w, lens=w.context_lens, seqs=range(3, w.num_seqs))
+    for P in (0, 64):
+        out = gpu_decode(pk, w, d, lens=lens, max_len=maxL, partition_size=P)
+        assert np.all(np.isnan(out[0])) and np.all(np.isnan(out[1]))
+        assert_parity(out, ref, w, seqs=range(3, w.num_seqs), what="rows next to invalid ones")
+    # an out-of-range table entry is never dereferenced; its rows become NaN
+    t = w.block_tables.copy()
+    t[2, 0] = w.num_blocks + 5
+    d.tables = torch.from_numpy(t).cuda()
+    for P in (0, 64):
+        out = gpu_decode(pk, w, d, partition_size=P)
+        assert np.all(np.isnan(out[2]))
+        assert_parity(out, ref, w, seqs=range(3, w.num_seqs), what="rows next to a bad table")
