@@ -1,0 +1,298 @@
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+A step is the whole path over one batch: slot mapping for every sequence's
+new token, the K/V append into its block, the fused score / online-softmax /
+V pass over every sequence's physical blocks, and the partition merge.  The
+workload is the Llama-7B-shaped decode batch (64 sequences, context lengths
+uniform in [128, 2048], 32 query / 32 kv heads, head_dim 128, bf16 K/V in
+16-token blocks dealt from a shuffled pool 1.25x the blocks in use).  Each
+step appends the token at position L and attends over L + 1 tokens.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+prints one JSON line: KV GB/s of the whole step (logical K+V bytes read by
+the attention, sum(L+1) * 2 * kv_heads * head_dim * 2 B, per step time), the
+roofline of the dominant kernel (the partition kernel, its duration from HIP
+events recorded around it on the launch stream inside the timed region), and
+the fp64 CPU oracle timed on the host's cores over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "paged decode attention: KV GB/s and % of MI355X HBM peak; seq-tokens/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama7b_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_357_amd", "csrc", f) for f in ("decode.hip", "pkv_internal.h")]
+
+WORKLOADS = {"llama7b-decode": 2, "tiny-f32": 1, "gqa-lognormal": 3, "cow-parallel-sampling": 4,
+             "long-context": 5}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b-decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--deal", default="shuffled", choices=["shuffled", "identity"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = all)")
+    ap.add_argument("--probes", action="store_true", help="also time plain HBM read / copy probes")
+    ap.add_argument("--flush-reps", type=int, default=0,
+                    help="also time this many single decode launches after a 1 GiB cache flush each")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="launch one plain copy of this size (reference kernel for byte counters)")
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(bytes_per_launch_algo: float, workload: str):
+    """HBM bytes per partition-kernel launch from the committed counter
+    summary, or None when it is missing, for another workload, or taken on a
+    different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"^\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_sha") != kernel_sha() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- CPU leg
+
+_CPU = {}
+
+
+def _cpu_worker(seqs):
+    from threadpoolctl import threadpool_limits
+    import oracle.paged_attention as pa
+    a = _CPU
+    with threadpool_limits(1):
+        pa.oracle_decode(a["q"], a["k"], a["v"], a["tables"], a["lens"], a["scale"], a["dtype"], a["B"], seqs=seqs)
+    return len(seqs)
+
+
+def cpu_baseline(w, lens, n_seqs):
+    """The fp64 oracle over (a sample of) the same decode, sequences spread
+    over a fork pool of the host's cores, one BLAS thread each."""
+    import multiprocessing as mp
+    from workloads import raw_numpy
+    seqs = list(range(w.num_seqs if n_seqs <= 0 else min(n_seqs, w.num_seqs)))
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), len(seqs)))
+    _CPU.update(q=raw_numpy(w.q), k=raw_numpy(w.k_cache), v=raw_numpy(w.v_cache), tables=w.block_tables,
+                lens=lens, scale=w.scale, dtype=w.dtype, B=w.block_size)
+    # longest first, dealt round robin, so the workers finish together
+    order = sorted(seqs, key=lambda s: -int(lens[s]))
+    chunks = [order[i::cores] for i in range(cores)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        done = sum(pool.map(_cpu_worker, chunks))
+    dt = time.perf_counter() - t0
+    assert done == len(seqs)
+    kv = w.kv_bytes(lens[seqs])
+    tokens = int(np.asarray(lens[seqs], dtype=np.int64).sum())
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle decode of sequences 0..{len(seqs) - 1} of {w.num_seqs} "
+                      f"({tokens} context tokens, all {w.q_heads} q heads) at the step's lengths L+1",
+            "seconds": dt, "seq_tokens_per_s": tokens / dt}
+
+
+# ---------------------------------------------------------------- GPU leg
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (the decode shards over "
+              "sequences or kv heads with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from workloads import make_config
+    k = WORKLOADS[args.workload]
+    w = make_config(k, deal=args.deal)
+    lens_step = (w.context_lens + 1).astype(np.int32)  # attend over the appended token too
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, lens_step, args.cpu_seqs)  # before the GPU is touched (fork pool)
+
+    import torch
+    import paged_kv_cache_357_amd as pk
+    pk.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, kc, vc = w.q.to(dev), w.k_cache.to(dev), w.v_cache.to(dev)
+    kn, vn = w.k_new.to(dev), w.v_new.to(dev)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    pos = torch.from_numpy(w.context_lens).to(dev)
+    lens = torch.from_numpy(lens_step).to(dev)
+    max_len = int(lens_step.max())
+    slots = torch.empty(w.num_seqs, dtype=torch.int32, device=dev)
+    call = pk.DecodeCall(q, kc, vc, tables, lens, w.scale, max_len, args.partition_size)
+    P, NP = call.plan
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pk.slot_mapping(tables, pos, w.num_blocks, w.block_size, out=slots)
+        pk.append(kc, vc, kn, vn, slots)
+        if ev is not None:
+            ev[1].record()
+        call.partitions()
+        if ev is not None:
+            ev[2].record()
+        call.reduce()
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    part_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    red_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    app_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+
+    kv_bytes = w.kv_bytes(lens_step)
+    tokens = int(lens_step.astype(np.int64).sum())
+    value = kv_bytes / (ms_step / 1e3) / 1e9
+    achieved = kv_bytes / (part_ms / 1e3) / 1e9
+    traffic = read_traffic(kv_bytes, args.workload)
+
+    extra = {
+        "kv_bytes_per_step": kv_bytes,
+        "pct_of_hbm_peak_step": 100.0 * value / HBM_PEAK_GBS,
+        "seq_tokens_per_s": tokens / (ms_step / 1e3),
+        "decode_tokens_per_s": w.num_seqs / (ms_step / 1e3),
+        "partition_kernel_ms": part_ms, "reduce_kernel_ms": red_ms, "slot_map_append_ms": app_ms,
+        "partition_size": P, "num_partitions": NP,
+        "kernel_sha": kernel_sha(),
+    }
+
+    if args.flush_reps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(args.flush_reps):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call.run()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        med = float(np.median(times))
+        extra["flushed_decode_ms_median"] = med
+        extra["flushed_decode_GBps"] = kv_bytes / (med / 1e3) / 1e9
+        del flush
+
+    if args.probes or args.copy_probe_mib:
+        import ctypes
+        plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_357_amd", "libpkv_probes.so"))
+        for fn in (plib.pkv_probe_copy, plib.pkv_probe_read, plib.pkv_probe_fill):
+            fn.restype = ctypes.c_int
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if args.copy_probe_mib:
+            nb = args.copy_probe_mib << 20
+            src = torch.empty(nb, dtype=torch.uint8, device=dev)
+            dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+            src.fill_(3)
+            torch.cuda.synchronize()
+            rc = plib.pkv_probe_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                     ctypes.c_size_t(nb), stream)
+            assert rc == 0
+            torch.cuda.synchronize()
+            extra["copy_probe_bytes"] = nb
+            del src, dst
+        if args.probes:
+            nb = 4 << 30
+            buf = torch.empty(nb, dtype=torch.uint8, device=dev)
+            buf.fill_(1)
+            dst = torch.empty(nb // 2, dtype=torch.uint8, device=dev)
+            sink = torch.zeros(4, dtype=torch.int32, device=dev)
+            res = {}
+            for name, fn in (("read", lambda: plib.pkv_probe_read(ctypes.c_void_p(buf.data_ptr()),
+                                                                 ctypes.c_size_t(nb),
+                                                                 ctypes.c_void_p(sink.data_ptr()), stream)),
+                             ("copy", lambda: plib.pkv_probe_copy(ctypes.c_void_p(dst.data_ptr()),
+                                                                 ctypes.c_void_p(buf.data_ptr()),
+                                                                 ctypes.c_size_t(nb // 2), stream))):
+                ts = []
+                for _ in range(6):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    assert fn() == 0
+                    b.record()
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                t = float(np.median(ts[1:]))
+                moved = nb if name == "read" else nb  # copy: nb/2 read + nb/2 written
+                res[name + "_GBps"] = moved / (t / 1e3) / 1e9
+            extra["probe"] = res
+            del buf, dst
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "num_seqs": w.num_seqs, "context_tokens_per_step": tokens,
+            "q_heads": w.q_heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+            "num_blocks": w.num_blocks, "block_layout": args.deal, "kv_dtype": w.dtype, "accumulate": "fp32",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": "decode_partition_kernel", "algorithmic_bytes_per_launch": kv_bytes,
+        },
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
