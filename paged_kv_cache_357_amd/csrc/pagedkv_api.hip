@@ -12,8 +12,6 @@
 
 namespace {
 
-constexpr int kMaxGridYZ = 65535;
-
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool valid_dtype(int dtype) { return dtype == PKV_DTYPE_F32 || dtype == PKV_DTYPE_BF16; }
@@ -22,18 +20,26 @@ int elt_bytes(int dtype) { return dtype == PKV_DTYPE_BF16 ? 2 : 4; }
 struct Plan {
   int P = 0;
   int NP = 0;
+  int n_units = 0;
+  int n_wg = 0;
+  int xcd_group = 0;
+  int grid = 0;
   size_t acc_bytes = 0;  // workspace region of partial accumulators
   size_t ml_bytes = 0;   // workspace region of partial (max, sum) pairs
   size_t total() const { return acc_bytes + ml_bytes; }
 };
 
+#ifndef PKV_AUTO_PARTITION
+#define PKV_AUTO_PARTITION 512
+#endif
+
 // Automatic partition size.  Sequences no longer than one partition are
-// finished in a single pass; longer ones are cut into 512-token partitions,
-// which bounds the work of one workgroup (so lengths that differ by 16x still
+// finished in a single pass; longer ones are cut into partitions of a fixed
+// size, which bounds the work of one wave (so lengths that differ by 16x still
 // spread evenly over the chip) at a merge cost of (D + 2) * 4 bytes per
 // partition and query head.
 int auto_partition(int max_len) {
-  constexpr int kDefault = 512;
+  constexpr int kDefault = PKV_AUTO_PARTITION;
   if (max_len <= kDefault) return max_len <= pkv::kChunk ? pkv::kChunk : (max_len + 15) / 16 * 16;
   return kDefault;
 }
@@ -47,7 +53,6 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
   if (!(group == 1 || group == 2 || group == 4 || group == 8 || group == 16)) return PKV_ERR_UNSUPPORTED;
   if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
   if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs > kMaxGridYZ || kv_heads > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
   int P = partition_size;
   if (P == 0) {
     P = auto_partition(max_context_len);
@@ -55,9 +60,21 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
     return PKV_ERR_UNSUPPORTED;
   }
   const long long np = max_context_len == 0 ? 1 : ((long long)max_context_len + P - 1) / P;
-  if (np > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  // one wave per (partition, sequence, kv head); ids and the launch grid are int
+  const long long units = np * num_seqs * kv_heads;
+  const long long n_wg = (units + pkv::kWavesPerWG - 1) / pkv::kWavesPerWG;
+  const long long seqs_grouped = num_seqs < pkv::kSeqGroup ? (num_seqs > 0 ? num_seqs : 1) : pkv::kSeqGroup;
+  long long xg = (seqs_grouped * kv_heads) / pkv::kWavesPerWG;
+  if (xg < 1) xg = 1;
+  const long long span = (long long)pkv::kXcds * xg;
+  const long long grid = (n_wg + span - 1) / span * span;
+  if (grid > 0x7fffffffLL || (long long)num_seqs * q_heads > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
   plan->P = P;
   plan->NP = (int)np;
+  plan->n_units = (int)units;
+  plan->n_wg = (int)n_wg;
+  plan->xcd_group = (int)xg;
+  plan->grid = (int)grid;
   if (plan->NP > 1) {
     const size_t rows = (size_t)num_seqs * q_heads * plan->NP;
     plan->acc_bytes = round_up(rows * head_dim * sizeof(float), 256);
@@ -98,6 +115,10 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   p->max_len = max_context_len;
   p->P = plan.P;
   p->NP = plan.NP;
+  p->n_units = plan.n_units;
+  p->n_wg = plan.n_wg;
+  p->xcd_group = plan.xcd_group;
+  p->grid = plan.grid;
   p->scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   return PKV_OK;
 }

@@ -7,14 +7,24 @@
 
 namespace pkv {
 
-// Tokens one wavefront consumes per loop iteration.  Block sizes are
-// multiples of it, so a chunk never straddles two physical blocks.
+// Tokens a wavefront consumes per step.  Block sizes are multiples of it, and
+// partitions start at multiples of it, so a chunk never straddles two
+// physical blocks.
 constexpr int kChunk = 16;
-// Largest partition (tokens) a decode workgroup covers; bounds the staged
-// block-table slice held in LDS.
+// Largest partition (tokens) one decode unit covers.
 constexpr int kMaxPartition = 8192;
-// Waves per decode workgroup.
-constexpr int kWaves = 4;
+// Waves per decode workgroup.  Each wave is an independent work unit.
+constexpr int kWavesPerWG = 4;
+// Accelerator complex dies of the MI355X; consecutive workgroup ids of a
+// launch are dealt round robin over them.
+constexpr int kXcds = 8;
+// Sequences whose tiles are kept together on one XCD (so that sequences
+// forked from one prompt, which are usually neighbours, read the shared
+// blocks through the same L2).
+#ifndef PKV_SEQ_GROUP
+#define PKV_SEQ_GROUP 4
+#endif
+constexpr int kSeqGroup = PKV_SEQ_GROUP;
 
 struct DecodeParams {
   float* out;             // [S, Hq, D]
@@ -26,6 +36,10 @@ struct DecodeParams {
   const int32_t* tables;  // [S, MB]
   const int32_t* lens;    // [S]
   int32_t S, Hq, Hkv, NB, MB, max_len, P, NP;
+  int32_t n_units;        // NP * S * Hkv decode units (one wave each)
+  int32_t n_wg;           // workgroups holding them: ceil(n_units / kWavesPerWG)
+  int32_t xcd_group;      // consecutive logical workgroups kept on one XCD (0: no remap)
+  int32_t grid;           // launched workgroups (>= n_wg; the surplus exits at once)
   float scale_log2;       // scale * log2(e): scores live in the base-2 domain
 };
 
