@@ -8,56 +8,62 @@
 // the Value rows.  Token i is read from slot T[i / B] * B + i % B
 // ("PagedAttention Paper Breakdown", section 2, Address Translation Formula).
 //
-// Work decomposition
-//   * A decode unit is (sequence s, kv head g, partition p): P consecutive
-//     logical tokens of one sequence for one kv head and its GQA group of
-//     query heads.  One wavefront (64 lanes) runs one unit from start to end;
-//     nothing is shared between the waves of a workgroup, so there is no LDS
-//     and no barrier.
-//   * Units are numbered ((p * S + s) * Hkv + g); workgroup l holds units
-//     4l .. 4l+3.  The hardware deals consecutive workgroup ids round robin
-//     over the 8 XCDs; the launch permutes ids so that the workgroups of a
-//     few neighbouring sequences (all their heads, one partition) run on the
-//     same XCD, one after the other, while successive such groups still
-//     alternate over the XCDs.  A token's K rows of all heads are then read
-//     through one L2, and sequences forked from one prompt share their
-//     prompt blocks in it.
-//   * A token's K (or V) row of one kv head is D * elt bytes (256 B for bf16
-//     D=128 and fp32 D=64).  LPT lanes cover it with one 16-byte load each, so
-//     one wave load instruction reads TPI = 64 / LPT whole rows and every lane
-//     keeps the same 16-byte column of the row for the whole unit.
-//   * The unit's slice of the block table sits in one VGPR (lane i holds the
-//     physical block of the unit's i-th logical block, 64 blocks per window);
-//     each 16-token chunk reads its block id with a lane read, so address
-//     computation never waits on memory.
-//   * K and V rows are fetched with nontemporal loads (they are read once),
-//     two chunks deep: the loads of chunk c+1 are in flight while chunk c is
-//     being consumed.
-//   * Scores: partial dot products of the 16-byte columns, finished with DPP
-//     adds across the LPT lanes of a row.  Each group of LPT lanes keeps its
-//     own online-softmax state (running max m, running sum l, accumulator of
-//     its columns); the groups are merged at the end of the unit with the
-//     log-sum-exp rule, and partitions are merged the same way by the second
-//     kernel.
-// Every reduction order depends only on logical token positions, never on
-// which physical block holds a token, so outputs are bitwise independent of
-// the block layout and bitwise reproducible.
+// Work is cut into 16-token chunks of one (sequence s, kv head g) segment; a
+// chunk lies inside one physical block, so its rows start at a wave-uniform
+// address.  One wavefront (64 lanes) is one worker: it streams its chunks
+// with the loads of the next chunk in flight while the current one is
+// consumed, keeps the online-softmax state of the kv head's GQA group of
+// query heads in registers, and at the end of each segment piece either
+// writes the finished rows or a partial (max, sum, accumulator) record that a
+// second kernel merges with the log-sum-exp rule.  The waves of a workgroup
+// share nothing (no LDS traffic in the loop, no barrier after the prologue).
 //
-// Masking: tokens at or beyond the unit's end inside its last chunk load the
-// row of its last token (always in bounds and written) and get score -inf,
-// hence weight exactly 0.  Running maxima start at -1e30 rather than -inf so
-// that a group that has seen no token yet rescales by exp2(0) = 1 instead of
+// Two schedules hand out the chunks:
+//   * balanced: all segments laid end to end, (s, g) in order, are cut into
+//     one equal share per worker wave, and the grid holds exactly as many
+//     waves as the chip keeps resident, so every wave starts at once and all
+//     finish together (no tail of long units started late).  A share may
+//     begin or end inside a segment; such pieces leave partial records (at
+//     most two per wave).  Each workgroup first builds the per-sequence chunk
+//     prefix sums in LDS to locate its shares.
+//   * partitioned: a unit is (s, g, partition p) of P consecutive tokens, one
+//     wave per unit, units numbered ((p * S + s) * Hkv + g); used when the
+//     caller fixes the partition size, when every sequence fits one
+//     partition, or for batches too long for the LDS tables.
+// In both, the hardware deals consecutive workgroup ids round robin over the
+// 8 XCDs; the launch permutes ids so that groups of consecutive logical
+// workgroups (neighbouring heads of the same tokens) share an XCD and its L2.
+//
+// Two compute cores consume a chunk:
+//   * ValuCore (fp32 caches, and bf16 with fewer than 4 query heads per kv
+//     head): a token row of one kv head is D * elt bytes; LPT lanes cover it
+//     with one 16-byte load each (one wave load instruction reads TPI =
+//     64 / LPT whole rows); partial dot products are finished with DPP adds
+//     across the LPT lanes; each lane group keeps its own softmax state, and
+//     the groups are merged at the end of a piece.
+//   * MfmaCore (bf16 with 4 or more query heads per kv head): scores and the
+//     V product are 16x16 matrix products on the matrix cores (see below).
+//
+// Every reduction order depends only on logical token positions and on the
+// lengths of the batch, never on which physical block holds a token, so
+// outputs are bitwise independent of the block layout and bitwise
+// reproducible.
+//
+// Masking: rows at or beyond a piece's end inside its last chunk are either
+// loaded from the piece's last row (ValuCore) or read as zero through a
+// bounds-checked buffer resource (MfmaCore); their scores are -inf, hence
+// weight exactly 0.  Running maxima start at -1e30 rather than -inf so that a
+// lane that has seen no token yet rescales by exp2(0) = 1 instead of
 // exp2(-inf + inf) = NaN.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
-#ifndef PKV_PREFETCH
-#define PKV_PREFETCH 1
-#endif
 #ifndef PKV_NT_LOADS
 #define PKV_NT_LOADS 1
 #endif
@@ -66,14 +72,41 @@ namespace pkv {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;
+constexpr int kThreads = kWavesPerWG * 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Cache-policy operand of the buffer loads: bit 1 is the nontemporal hint.
+constexpr int kStreamPolicy = PKV_NT_LOADS ? 2 : 0;
+// Fourth word of a raw buffer resource on gfx9-family parts (gfx950).
+constexpr int kBufferConfig = 0x00020000;
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reinterpret one 32-bit word as two bf16.  The word is taken by value: a
+// bit cast applied directly to an element of an ext_vector_type value (k.y)
+// has been seen to read element 0 instead, so vector elements always go
+// through this copy.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+__device__ __forceinline__ u32x4 make_u32x4(const uint4& t) { return u32x4{t.x, t.y, t.z, t.w}; }
+__device__ __forceinline__ u32x2 make_u32x2(uint32_t x, uint32_t y) { return u32x2{x, y}; }
+
+// Two floats rounded to bf16 (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // One 16-byte column of a K or V row.  The rows are streamed once per call,
 // so they are fetched with the nontemporal hint.
@@ -102,45 +135,6 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-// Reinterpret one 32-bit word as two bf16.  The word is taken by value: a
-// bit cast applied directly to an element of an ext_vector_type value (k.y)
-// has been seen to read element 0 instead, so vector elements always go
-// through this copy.
-__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
-
-// Partial dot product of one lane's 16-byte column of q and of a K row.
-template <int DT>
-__device__ __forceinline__ float dot16(const uint32_t (&q)[4], const u32x4& k) {
-  if constexpr (DT == 1) {
-    const uint32_t k0 = k.x, k1 = k.y, k2 = k.z, k3 = k.w;
-    float d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[0]), as_bf16x2(k0), 0.0f, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[1]), as_bf16x2(k1), d, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[2]), as_bf16x2(k2), d, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[3]), as_bf16x2(k3), d, false);
-    return d;
-  } else {
-    float d = __uint_as_float(q[0]) * __uint_as_float(k.x);
-    d = fmaf(__uint_as_float(q[1]), __uint_as_float(k.y), d);
-    d = fmaf(__uint_as_float(q[2]), __uint_as_float(k.z), d);
-    d = fmaf(__uint_as_float(q[3]), __uint_as_float(k.w), d);
-    return d;
-  }
-}
-
-// The EPL values of one lane's 16-byte column of a V row, widened to fp32.
-template <int DT>
-__device__ __forceinline__ void widen16(const u32x4& v, float* f) {
-  if constexpr (DT == 1) {
-    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-  } else {
-    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
-  }
-}
-
 // Logical workgroup index of launched workgroup b, or -1 for the surplus.
 // Launched workgroup b runs on XCD b % 8.  Logical workgroups are taken in
 // groups of `group` consecutive ids; group k runs on XCD k % 8, its members
@@ -153,9 +147,9 @@ __device__ __forceinline__ int logical_workgroup(int b, int group, int n_wg) {
   return l < n_wg ? l : -1;
 }
 
-// Physical block ids of logical blocks base .. base+63 of the unit, one per
-// lane (0 past the unit's last block).  An id outside [0, NB) is replaced by 0
-// so it is never dereferenced, and reported through *bad.
+// Physical block ids of logical blocks base .. base+63 of a sequence, one
+// per lane (0 past its last block).  An id outside [0, NB) is replaced by 0 so
+// it is never dereferenced, and reported through *bad.
 __device__ __forceinline__ int load_table_window(const int32_t* trow, int base, int n_blk, int lane, int NB,
                                                  bool* bad) {
   int b = 0;
@@ -165,112 +159,131 @@ __device__ __forceinline__ int load_table_window(const int32_t* trow, int base, 
   return ok ? b : 0;
 }
 
+// Where the output of a finished piece goes.  Direct: the G rows of out
+// starting at `out` (D floats apart).  Partial: G accumulator rows starting at
+// `acc` (acc_stride rows apart) and their (max, sum) pairs at `ml`
+// (ml_stride apart).
+struct PieceSink {
+  bool direct;
+  bool bad;
+  float* out;
+  float* acc;
+  size_t acc_stride;
+  float2* ml;
+  size_t ml_stride;
+};
+
+// --------------------------------------------------------------- ValuCore
+
 template <int DT, int D, int B, int G>
-__global__ __launch_bounds__(kWavesPerWG * 64) void decode_units_kernel(DecodeParams a) {
-  constexpr int ELT = DT == 1 ? 2 : 4;
-  constexpr int EPL = 16 / ELT;         // elements per lane per row
-  constexpr int LPT = D / EPL;          // lanes per token row
-  constexpr int TPI = 64 / LPT;         // token rows per wave load instruction
-  constexpr int NI = kChunk / TPI;      // load instructions per tensor per chunk
-  constexpr int ROW = D * ELT;          // bytes of one token row of one kv head
+struct ValuCore {
+  static constexpr int ELT = DT == 1 ? 2 : 4;
+  static constexpr int EPL = 16 / ELT;      // elements per lane per row
+  static constexpr int LPT = D / EPL;       // lanes per token row
+  static constexpr int TPI = 64 / LPT;      // token rows per wave load instruction
+  static constexpr int NI = kChunk / TPI;   // load instructions per tensor per chunk
+  static constexpr int ROW = D * ELT;       // bytes of one token row of one kv head
+  static constexpr int kBlock = B;
+  static constexpr int kHeadDim = D;
+  static constexpr int kGroup = G;
+  static constexpr int kWavesPerSimd = balanced_waves_per_simd(DT, D, G);
   static_assert(LPT == 8 || LPT == 16 || LPT == 32, "row must span 8, 16 or 32 lanes");
   static_assert(B % kChunk == 0, "block size must be a multiple of the chunk");
 
-  const int ell = logical_workgroup(blockIdx.x, a.xcd_group, a.n_wg);
-  if (ell < 0) return;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u = ell * kWavesPerWG + wave;
-  if (u >= a.n_units) return;
-  const int lane = threadIdx.x & 63;
-  const int g = u % a.Hkv;
-  const int sp = u / a.Hkv;
-  const int s = sp % a.S;
-  const int part = sp / a.S;
+  struct Buf {
+    u32x4 k[NI], v[NI];
+  };
 
-  const int L = a.lens[s];
-  const int tok0 = part * a.P;
-  const bool bad_len = (L < 0) || (L > a.max_len);
-  const bool direct = (L <= a.P);  // this sequence fits one partition: write out directly
-  float* orow = a.out + ((size_t)s * a.Hq + (size_t)g * G) * D;
+  int grp, seg;
+  uint32_t q[G][4], qn[G][4];
+  float m[G], l[G], acc[G][EPL];
 
-  if (bad_len || tok0 >= L) {
-    // Nothing to attend to.  The partition-0 unit owns the output rows of
-    // sequences handled directly (L = 0 gives zeros, a bad length NaN);
-    // otherwise the merge kernel writes them.
-    if (part == 0 && (bad_len || direct)) {
-      const float fill = bad_len ? __builtin_nanf("") : 0.0f;
-      for (int i = lane; i < G * D; i += 64) orow[i] = fill;
-    }
-    return;
+  __device__ void init(int lane, uint32_t /*rs*/) {
+    grp = lane / LPT;
+    seg = lane % LPT;
   }
 
-  const int grp = lane / LPT;
-  const int seg = lane % LPT;
-  const int tok_end = min(tok0 + a.P, L);
-  const int n_chunks = (tok_end - tok0 + kChunk - 1) / kChunk;
-  const int blk0 = tok0 / B;
-  const int n_blk = (tok_end - 1) / B - blk0 + 1;
-  const int32_t* trow = a.tables + (size_t)s * a.MB + blk0;
+  __device__ void reset() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = kNegBig;
+      l[h] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+    }
+  }
 
-  bool bad_blk = false;
-  int wbase = 0;
-  int tbl = load_table_window(trow, 0, n_blk, lane, a.NB, &bad_blk);
-
-  uint32_t qw[G][4];
-  {
+  // Query rows of heads g*G .. g*G+G-1 of sequence s: this lane's column.
+  __device__ void fetch_q(const DecodeParams& a, int s, int g, bool into_next) {
     const char* qsrc = static_cast<const char*>(a.q) + ((size_t)s * a.Hq + (size_t)g * G) * ROW + seg * 16;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const uint4 t = *reinterpret_cast<const uint4*>(qsrc + h * ROW);
-      qw[h][0] = t.x; qw[h][1] = t.y; qw[h][2] = t.z; qw[h][3] = t.w;
+      uint32_t* d = into_next ? qn[h] : q[h];
+      d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
     }
   }
 
-  float m[G], l[G], acc[G][EPL];
+  __device__ void take_next_q() {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegBig;
-    l[h] = 0.0f;
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+      for (int i = 0; i < 4; ++i) q[h][i] = qn[h][i];
   }
 
-  const uint32_t row_stride = (uint32_t)a.Hkv * ROW;  // bytes between slots of one head
-  const char* kbase = static_cast<const char*>(a.k) + (size_t)g * ROW + seg * 16;
-  const char* vbase = static_cast<const char*>(a.v) + (size_t)g * ROW + seg * 16;
-  const float sl2 = a.scale_log2;
-
-  // Issue the K and V loads of chunk c.
-  auto issue = [&](int c, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
-    const int cs = tok0 + c * kChunk;
-    const int bi = cs / B - blk0;
-    if (bi - wbase >= 64) {
-      wbase += 64;
-      tbl = load_table_window(trow, wbase, n_blk, lane, a.NB, &bad_blk);
-    }
-    const int phys = __builtin_amdgcn_readlane(tbl, bi - wbase);
-    const size_t cbase = ((size_t)phys * B + (size_t)(cs % B)) * row_stride;
-    const int lim = tok_end - 1 - cs;  // last valid row of the chunk
+  // Loads of one chunk: kc / vc point at the chunk's first row of this kv
+  // head; rows past `lim` repeat row `lim`.
+  __device__ void issue(const char* kc, const char* vc, uint32_t rs, int lim, Buf& b) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t t = (uint32_t)min(i * TPI + grp, lim);
-      kr[i] = load_row16(kbase + cbase + t * row_stride);
+      b.k[i] = load_row16(kc + t * rs + seg * 16);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t t = (uint32_t)min(i * TPI + grp, lim);
-      vr[i] = load_row16(vbase + cbase + t * row_stride);
+      b.v[i] = load_row16(vc + t * rs + seg * 16);
     }
-  };
+  }
 
-  // Scores, online softmax and V accumulation of chunk c.
-  auto consume = [&](int c, const u32x4 (&kr)[NI], const u32x4 (&vr)[NI]) {
-    const int lim = tok_end - 1 - (tok0 + c * kChunk);
+  // Partial dot product of this lane's 16-byte column of q and of a K row.
+  __device__ float dot16(const uint32_t (&qh)[4], const u32x4& k) const {
+    if constexpr (DT == 1) {
+      const uint32_t k0 = k.x, k1 = k.y, k2 = k.z, k3 = k.w;
+      float d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qh[0]), as_bf16x2(k0), 0.0f, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qh[1]), as_bf16x2(k1), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qh[2]), as_bf16x2(k2), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qh[3]), as_bf16x2(k3), d, false);
+      return d;
+    } else {
+      float d = __uint_as_float(qh[0]) * __uint_as_float(k.x);
+      d = fmaf(__uint_as_float(qh[1]), __uint_as_float(k.y), d);
+      d = fmaf(__uint_as_float(qh[2]), __uint_as_float(k.z), d);
+      d = fmaf(__uint_as_float(qh[3]), __uint_as_float(k.w), d);
+      return d;
+    }
+  }
+
+  // The EPL values of this lane's 16-byte column of a V row, widened to fp32.
+  __device__ void widen16(const u32x4& v, float* f) const {
+    if constexpr (DT == 1) {
+      f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+      f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+      f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+      f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+    } else {
+      f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+      f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    }
+  }
+
+  // Scores, online softmax and V accumulation of one chunk (rows 0 .. lim valid).
+  __device__ void consume(int lim, float sl2, const Buf& b) {
     float p[G][NI];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) p[h][i] = row_sum<LPT>(dot16<DT>(qw[h], kr[i]));
+      for (int i = 0; i < NI; ++i) p[h][i] = row_sum<LPT>(dot16(q[h], b.k[i]));
 
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -297,99 +310,363 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void decode_units_kernel(DecodePa
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[EPL];
-      widen16<DT>(vr[i], vf);
+      widen16(b.v[i], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p[h][i], vf[e], acc[h][e]);
     }
+  }
+
+  // Merge the TPI lane groups, then write the piece.  Lane group 0 holds the
+  // merged columns seg * EPL .. seg * EPL + EPL - 1.
+  __device__ void finish(const PieceSink& o) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float M = m[h];
+#pragma unroll
+      for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float w = fast_exp2(m[h] - M);
+      float lw = l[h] * w;
+#pragma unroll
+      for (int off = LPT; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float aw = acc[h][e] * w;
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) aw += __shfl_xor(aw, off);
+        acc[h][e] = aw;
+      }
+      m[h] = M;
+      l[h] = lw;
+    }
+    if (grp != 0) return;
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (o.direct) {
+        float4* dst = reinterpret_cast<float4*>(o.out + h * D + seg * EPL);
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          dst[e / 4] = o.bad ? make_float4(nan, nan, nan, nan)
+                             : make_float4(acc[h][e] / l[h], acc[h][e + 1] / l[h], acc[h][e + 2] / l[h],
+                                           acc[h][e + 3] / l[h]);
+      } else {
+        float4* dst = reinterpret_cast<float4*>(o.acc + h * o.acc_stride * D + seg * EPL);
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          dst[e / 4] = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+        if (seg == 0) o.ml[h * o.ml_stride] = o.bad ? make_float2(INFINITY, nan) : make_float2(m[h], l[h]);
+      }
+    }
+  }
+};
+
+// --------------------------------------------------------------- MfmaCore
+//
+// The 16 token slots of a chunk are the rows of two small matrix products,
+// computed with MFMA instructions (64 lanes, 16x16 tiles; lane l has lane
+// group gl = l / 16 and column cl = l % 16):
+//   scores  S[t][h] = sum_d K[t][d] q[h][d]          v_mfma_f32_16x16x32_bf16
+//           A = K (row t = cl; its k values are the 16-byte column
+//           gl + 4j of token t's row in step j), B = q^T (column h = cl,
+//           query head h of the group, zero for h >= G).  The result puts
+//           slots 4 gl + r (r = 0..3) of head cl in lane l.
+//   output  O^T[d][h] += sum_t V[t][d] P[h][t]       v_mfma_f32_16x16x16_bf16
+//           A = V^T (row cl is column CW cl + dt of the row, tile dt; its four
+//           k values are token slots 4 gl + r), B = P^T, which is exactly
+//           the layout the score product left in the registers.
+// Both operands of a product assign the contraction index through the same
+// lane-to-k rule, so every d (and every token slot) is paired with itself.
+// The softmax weights P are fp32; they enter the bf16 product split into a
+// high part (the top 16 bits) and a low part (the rest, rounded to bf16), so
+// the weight carried into the fp32 accumulation is within 2^-16 of P.  V and
+// K are bf16 inputs and enter exactly.
+//
+// Each lane keeps the online-softmax state of its head cl over its own four
+// token slots; the running maximum is shared by the four lane groups (one
+// cross-group max per chunk), so the matrix product adds their terms
+// directly.  The accumulator is rescaled only when some running maximum grew
+// (a factor of exactly 1 is skipped, which changes nothing).
+//
+// K and V rows are fetched with buffer loads whose resource covers only the
+// chunk's valid rows: rows past the piece's end read as zero and take no
+// memory traffic; their scores are masked to -inf.
+
+template <int D, int B, int G>
+struct MfmaCore {
+  static constexpr int ROW = D * 2;        // bytes of one token row of one kv head
+  static constexpr int KSTEPS = D / 32;    // score products per chunk
+  static constexpr int CW = D / 16;        // bf16 of a V row per lane (8 or 4) = output tiles
+  static constexpr int kBlock = B;
+  static constexpr int kHeadDim = D;
+  static constexpr int kGroup = G;
+  static constexpr int kWavesPerSimd = balanced_waves_per_simd(1, D, G);
+  static_assert(G <= 16, "a group must fit the 16 columns of a tile");
+  static_assert(B % kChunk == 0, "block size must be a multiple of the chunk");
+  using VRow = typename std::conditional<CW == 8, u32x4, u32x2>::type;
+
+  struct Buf {
+    u32x4 k[KSTEPS];
+    VRow v[4];
   };
 
-  u32x4 ka[NI], va[NI];
-  issue(0, ka, va);
-#if PKV_PREFETCH
-  u32x4 kb[NI], vb[NI];
-  for (int c = 0; c < n_chunks; c += 2) {
-    if (c + 1 < n_chunks) issue(c + 1, kb, vb);
-    consume(c, ka, va);
-    if (c + 1 < n_chunks) {
-      if (c + 2 < n_chunks) issue(c + 2, ka, va);
-      consume(c + 1, kb, vb);
-    }
-  }
-#else
-  for (int c = 0; c < n_chunks; ++c) {
-    if (c > 0) issue(c, ka, va);
-    consume(c, ka, va);
-  }
-#endif
+  int gl, cl;
+  uint32_t koff, voff;
+  bf16x8 q[KSTEPS], qn[KSTEPS];
+  f32x4 acc[CW];
+  float m_run, l_run;
 
-  // Merge the TPI lane groups of the wave.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float M = m[h];
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float w = fast_exp2(m[h] - M);
-    float lw = l[h] * w;
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float aw = acc[h][e] * w;
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) aw += __shfl_xor(aw, off);
-      acc[h][e] = aw;
-    }
-    m[h] = M;
-    l[h] = lw;
+  __device__ void init(int lane, uint32_t rs) {
+    gl = lane >> 4;
+    cl = lane & 15;
+    koff = (uint32_t)cl * rs + 16u * (uint32_t)gl;             // + 64 j
+    voff = (uint32_t)(4 * gl) * rs + (uint32_t)cl * (2 * CW);   // + r rs
   }
 
-  // Finish (one partition) or write the partition's partials.  Lane group 0
-  // holds the merged columns seg * EPL .. seg * EPL + EPL - 1.
-  if (grp != 0) return;
-  if (direct) {
+  __device__ void reset() {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float o[EPL];
+    for (int dt = 0; dt < CW; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run = kNegBig;
+    l_run = 0.0f;
+  }
+
+  // q^T operand: column cl is query head g*G + cl of the group.
+  __device__ void fetch_q(const DecodeParams& a, int s, int g, bool into_next) {
+    const char* qsrc = static_cast<const char*>(a.q) + ((size_t)s * a.Hq + (size_t)g * G + cl) * ROW;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = bad_blk ? __builtin_nanf("") : acc[h][e] / l[h];
-      float4* dst = reinterpret_cast<float4*>(orow + h * D + seg * EPL);
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4) dst[e / 4] = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+    for (int j = 0; j < KSTEPS; ++j) {
+      uint4 t = make_uint4(0, 0, 0, 0);
+      if (cl < G) t = *reinterpret_cast<const uint4*>(qsrc + 16 * (gl + 4 * j));
+      const bf16x8 v = __builtin_bit_cast(bf16x8, make_u32x4(t));
+      if (into_next) qn[j] = v; else q[j] = v;
     }
-  } else {
+  }
+
+  __device__ void take_next_q() {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const size_t r = ((size_t)s * a.Hq + (size_t)g * G + h) * a.NP + part;
-      float4* dst = reinterpret_cast<float4*>(a.ws_acc + r * D + seg * EPL);
+    for (int j = 0; j < KSTEPS; ++j) q[j] = qn[j];
+  }
+
+  __device__ void issue(const char* kc, const char* vc, uint32_t rs, int lim, Buf& b) const {
+    const uint32_t nbytes = (uint32_t)lim * rs + ROW;  // rows 0 .. lim of this head
+    const __amdgpu_buffer_rsrc_t kres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kc), 0, (int)nbytes, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t vres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vc), 0, (int)nbytes, kBufferConfig);
 #pragma unroll
-      for (int e = 0; e < EPL; e += 4) {
-        dst[e / 4] = bad_blk ? make_float4(__builtin_nanf(""), 0.0f, 0.0f, 0.0f)
-                             : make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+    for (int j = 0; j < KSTEPS; ++j)
+      b.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, (int)(koff + 64u * j), 0,
+                                                                               kStreamPolicy));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (CW == 8)
+        b.v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)(voff + r * rs), 0,
+                                                                                 kStreamPolicy));
+      else
+        b.v[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vres, (int)(voff + r * rs), 0,
+                                                                                kStreamPolicy));
+    }
+  }
+
+  __device__ void consume(int lim, float sl2, const Buf& b) {
+    f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[j]), q[j], sc, 0, 0, 0);
+
+    float x[4];
+    float mx = m_run;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = (4 * gl + r <= lim) ? sc[r] * sl2 : -INFINITY;
+      mx = fmaxf(mx, x[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float alpha = fast_exp2(m_run - mx);
+    m_run = mx;
+    float p[4];
+    float ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = fast_exp2(x[r] - mx);
+      ps += p[r];
+    }
+    l_run = fmaf(l_run, alpha, ps);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < CW; ++dt) acc[dt] *= alpha;
+    }
+
+    // P^T operand, high and low bf16 parts.
+    uint32_t hb[4];
+    float res[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hb[r] = __float_as_uint(p[r]) & 0xffff0000u;
+      res[r] = p[r] - __uint_as_float(hb[r]);
+    }
+    const s16x4 phi = __builtin_bit_cast(s16x4, make_u32x2((hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3]));
+    const s16x4 plo =
+        __builtin_bit_cast(s16x4, make_u32x2(pack_bf16_rne(res[0], res[1]), pack_bf16_rne(res[2], res[3])));
+
+#pragma unroll
+    for (int dt = 0; dt < CW; ++dt) {
+      // element dt of token slots 4 gl + 0..3
+      const uint32_t w0 = b.v[0][dt / 2], w1 = b.v[1][dt / 2], w2 = b.v[2][dt / 2], w3 = b.v[3][dt / 2];
+      uint32_t lo, hi;
+      if (dt % 2 == 0) {
+        lo = (w0 & 0xffffu) | (w1 << 16);
+        hi = (w2 & 0xffffu) | (w3 << 16);
+      } else {
+        lo = (w0 >> 16) | (w1 & 0xffff0000u);
+        hi = (w2 >> 16) | (w3 & 0xffff0000u);
       }
-      if (seg == 0) a.ws_ml[r] = bad_blk ? make_float2(INFINITY, __builtin_nanf("")) : make_float2(m[h], l[h]);
+      const s16x4 vt = __builtin_bit_cast(s16x4, make_u32x2(lo, hi));
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, acc[dt], 0, 0, 0);
     }
   }
+
+  // Lane (gl, cl) holds head cl, columns CW * (4 gl + r) + dt: 4 * CW
+  // consecutive columns starting at 4 * CW * gl, in the order r * CW + dt.
+  // The four lane groups share m_run; their sums add.
+  __device__ void finish(const PieceSink& o) {
+    float lt = l_run + __shfl_xor(l_run, 16);
+    lt += __shfl_xor(lt, 32);
+    if (cl >= G) return;
+    float v[4 * CW];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int dt = 0; dt < CW; ++dt) v[r * CW + dt] = acc[dt][r];
+    const int col0 = 4 * CW * gl;
+    const float nan = __builtin_nanf("");
+    if (o.direct) {
+      float4* dst = reinterpret_cast<float4*>(o.out + cl * D + col0);
+#pragma unroll
+      for (int e = 0; e < 4 * CW; e += 4)
+        dst[e / 4] = o.bad ? make_float4(nan, nan, nan, nan)
+                           : make_float4(v[e] / lt, v[e + 1] / lt, v[e + 2] / lt, v[e + 3] / lt);
+    } else {
+      float4* dst = reinterpret_cast<float4*>(o.acc + cl * o.acc_stride * D + col0);
+#pragma unroll
+      for (int e = 0; e < 4 * CW; e += 4) dst[e / 4] = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+      if (gl == 0) o.ml[cl * o.ml_stride] = o.bad ? make_float2(INFINITY, nan) : make_float2(m_run, lt);
+    }
+  }
+};
+
+// ---------------------------------------------------- partitioned schedule
+
+template <class Core>
+__global__ __launch_bounds__(kThreads) void decode_partitioned_kernel(DecodeParams a) {
+  constexpr int B = Core::kBlock, D = Core::kHeadDim, G = Core::kGroup, ROW = Core::ROW;
+  const int ell = logical_workgroup(blockIdx.x, a.xcd_group, a.n_wg);
+  if (ell < 0) return;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int u = ell * kWavesPerWG + wave;
+  if (u >= a.n_units) return;
+  const int lane = threadIdx.x & 63;
+  const int g = u % a.Hkv;
+  const int sp = u / a.Hkv;
+  const int s = sp % a.S;
+  const int part = sp / a.S;
+
+  const int L = a.lens[s];
+  const int tok0 = part * a.P;
+  const bool bad_len = (L < 0) || (L > a.max_len);
+  const bool direct = (L <= a.P);  // this sequence fits one partition: write out directly
+  float* orow = a.out + ((size_t)s * a.Hq + (size_t)g * G) * D;
+
+  if (bad_len || tok0 >= L) {
+    // Nothing to attend to.  The partition-0 unit owns the output rows of
+    // sequences handled directly (L = 0 gives zeros, a bad length NaN);
+    // otherwise the merge kernel writes them.
+    if (part == 0 && (bad_len || direct)) {
+      const float fill = bad_len ? __builtin_nanf("") : 0.0f;
+      for (int i = lane; i < G * D; i += 64) orow[i] = fill;
+    }
+    return;
+  }
+
+  const int tok_end = min(tok0 + a.P, L);
+  const int n_chunks = (tok_end - tok0 + kChunk - 1) / kChunk;
+  const int blk0 = tok0 / B;
+  const int n_blk = (tok_end - 1) / B - blk0 + 1;
+  const int32_t* trow = a.tables + (size_t)s * a.MB + blk0;
+  const uint32_t rs = (uint32_t)a.Hkv * ROW;  // bytes between slots of one head
+  const char* kbase = static_cast<const char*>(a.k) + (size_t)g * ROW;
+  const char* vbase = static_cast<const char*>(a.v) + (size_t)g * ROW;
+
+  Core core;
+  core.init(lane, rs);
+  bool bad = false;
+  int wbase = 0;
+  int tbl = load_table_window(trow, 0, n_blk, lane, a.NB, &bad);
+  core.fetch_q(a, s, g, false);
+  core.reset();
+
+  auto issue = [&](int c, typename Core::Buf& b) {
+    const int cs = tok0 + c * kChunk;
+    const int bi = cs / B - blk0;
+    if (bi - wbase >= 64) {
+      wbase += 64;
+      tbl = load_table_window(trow, wbase, n_blk, lane, a.NB, &bad);
+    }
+    const int phys = __builtin_amdgcn_readlane(tbl, bi - wbase);
+    const size_t cbase = ((size_t)phys * B + (size_t)(cs % B)) * rs;
+    core.issue(kbase + cbase, vbase + cbase, rs, tok_end - 1 - cs, b);
+  };
+
+  typename Core::Buf ba, bb;
+  issue(0, ba);
+  for (int c = 0; c < n_chunks; c += 2) {
+    if (c + 1 < n_chunks) issue(c + 1, bb);
+    core.consume(tok_end - 1 - (tok0 + c * kChunk), a.scale_log2, ba);
+    if (c + 1 < n_chunks) {
+      if (c + 2 < n_chunks) issue(c + 2, ba);
+      core.consume(tok_end - 1 - (tok0 + (c + 1) * kChunk), a.scale_log2, bb);
+    }
+  }
+
+  PieceSink o;
+  o.direct = direct;
+  o.bad = bad;
+  o.out = orow;
+  const size_t r0 = ((size_t)s * a.Hq + (size_t)g * G) * a.NP + part;  // head 0 of the group
+  o.acc = a.ws_acc + r0 * D;
+  o.acc_stride = (size_t)a.NP;
+  o.ml = a.ws_ml + r0;
+  o.ml_stride = (size_t)a.NP;
+  core.finish(o);
 }
 
-// Stage 2: merge the partitions of sequences longer than one partition.
-// One wave per (sequence, query head).  Partition p contributes
-// exp2(m_p - M) * (acc_p, l_p), M the largest m_p; partitions are visited in
-// increasing order.  Lane j owns columns j*CPL .. j*CPL + CPL - 1.
+// Stage 2 of the partitioned schedule: merge the partitions of sequences
+// longer than one partition.  One workgroup of 4 waves per (sequence, query
+// head).  Partition p contributes exp2(m_p - M) * (acc_p, l_p), M the largest
+// m_p.  Wave w sums a contiguous quarter of the partitions in increasing
+// order, then wave 0 adds the four partial sums in wave order.  Lane j owns
+// columns j*CPL .. j*CPL + CPL - 1.
 template <int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams a) {
+__global__ __launch_bounds__(kThreads) void decode_reduce_partitioned_kernel(DecodeParams a) {
   constexpr int CPL = D / 64;  // columns per lane (1 or 2)
+  __shared__ float s_num[kWavesPerWG][D];
+  __shared__ float s_den[kWavesPerWG];
   const int row = blockIdx.x;  // s * Hq + h
   const int s = row / a.Hq;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
   const int L = a.lens[s];
   const bool bad_len = (L < 0) || (L > a.max_len);
-  if (!bad_len && L <= a.P) return;  // written by stage 1 (or L = 0 zeros)
+  if (!bad_len && L <= a.P) return;  // written by stage 1 (or L = 0 zeros); uniform over the workgroup
   float* o = a.out + (size_t)row * D + lane * CPL;
   if (bad_len) {
+    if (wave == 0) {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) o[j] = __builtin_nanf("");
+      for (int j = 0; j < CPL; ++j) o[j] = __builtin_nanf("");
+    }
     return;
   }
   const int np = (L + a.P - 1) / a.P;
@@ -401,18 +678,20 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
+  const int p_begin = (int)((long long)np * wave / kWavesPerWG);
+  const int p_end = (int)((long long)np * (wave + 1) / kWavesPerWG);
   float den = 0.0f;
   float num[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) num[j] = 0.0f;
-  for (int p0 = 0; p0 < np; p0 += 64) {
+  for (int p0 = p_begin; p0 < p_end; p0 += 64) {
     float f = 0.0f;
-    if (p0 + lane < np) {
+    if (p0 + lane < p_end) {
       const float2 t = ml[p0 + lane];
       f = fast_exp2(t.x - M);
       den = fmaf(t.y, f, den);
     }
-    const int cnt = min(64, np - p0);
+    const int cnt = min(64, p_end - p0);
     const float* ap = acc + (size_t)p0 * D;
     // eight partitions per step, so eight loads are in flight at once
     for (int j0 = 0; j0 < cnt; j0 += 8) {
@@ -434,6 +713,285 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams a) {
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) s_num[wave][lane * CPL + j] = num[j];
+  if (lane == 0) s_den[wave] = den;
+  __syncthreads();
+  if (wave != 0) return;
+  float tn[CPL], td = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) tn[j] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWavesPerWG; ++w) {
+    td += s_den[w];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) tn[j] += s_num[w][lane * CPL + j];
+  }
+  if constexpr (CPL == 2) {
+    *reinterpret_cast<float2*>(o) = make_float2(tn[0] / td, tn[1] / td);
+  } else {
+    o[0] = tn[0] / td;
+  }
+}
+
+// ------------------------------------------------------- balanced schedule
+//
+// Segment (s, g) holds n_s = ceil(L_s / 16) chunks (0 for L_s <= 0 or an
+// invalid length); segments are laid out in (s, g) order, so segment (s, g)
+// starts at chunk Hkv * C_s + g * n_s, C_s = n_0 + .. + n_{s-1}, and the
+// whole batch is T = Hkv * C_S chunks.  With W worker waves (W_eff = min(W,
+// max(1, T / kBalancedMinChunks)) of them get work), wave w takes chunks
+// [w T / W_eff, (w+1) T / W_eff).  A piece of a segment that this wave both
+// starts and ends is written directly; otherwise the wave leaves a partial
+// record in slot 0 (the piece continues a segment begun by an earlier wave)
+// or slot 1 (the piece begins a segment that a later wave continues).
+
+// Wave whose share contains chunk c.
+__device__ __forceinline__ long long balanced_wave_of(long long c, long long T, long long W_eff) {
+  return ((c + 1) * W_eff - 1) / T;
+}
+
+__device__ __forceinline__ long long balanced_workers(long long T, int W) {
+  long long w = T / kBalancedMinChunks;
+  if (w > W) w = W;
+  return w < 1 ? 1 : w;
+}
+
+template <class Core>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Core::kWavesPerSimd)))
+void decode_balanced_kernel(DecodeParams a) {
+  constexpr int B = Core::kBlock, D = Core::kHeadDim, G = Core::kGroup, ROW = Core::ROW;
+  extern __shared__ int smem[];
+  int* pref = smem;               // [S + 1] chunk prefix sums C_s
+  int* slen = smem + a.S + 1;     // [S] lengths (0 for invalid ones)
+  __shared__ int s_wave_sum[kWavesPerWG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+
+  // Per-sequence chunk counts and their exclusive prefix sums.
+  {
+    const int per = (a.S + kThreads - 1) / kThreads;
+    const int s_lo = min(a.S, tid * per);
+    const int s_hi = min(a.S, s_lo + per);
+    int local = 0;
+    for (int s = s_lo; s < s_hi; ++s) {
+      const int L = a.lens[s];
+      const int Lv = (L > 0 && L <= a.max_len) ? L : 0;
+      slen[s] = Lv;
+      local += (Lv + kChunk - 1) / kChunk;
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) s_wave_sum[wave] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += s_wave_sum[w];
+    for (int s = s_lo; s < s_hi; ++s) {
+      pref[s] = run;
+      run += (slen[s] + kChunk - 1) / kChunk;
+    }
+    if (tid == kThreads - 1) pref[a.S] = run;
+    __syncthreads();
+  }
+  if (blockIdx.x == 0)
+    for (int s = tid; s <= a.S; s += kThreads) a.ws_pref[s] = pref[s];
+
+  const int Hkv = a.Hkv;
+  const long long T = (long long)Hkv * uniform(pref[a.S]);
+  const int ell = logical_workgroup(blockIdx.x, a.xcd_group, a.n_wg);
+  if (ell < 0 || T == 0) return;
+  const long long W_eff = balanced_workers(T, a.n_units);
+  const int w = ell * kWavesPerWG + wave;
+  if (w >= W_eff) return;
+  const long long lo = (long long)w * T / W_eff;
+  const long long hi = (long long)(w + 1) * T / W_eff;
+
+  // Locate the segment holding chunk lo: the last s with Hkv * C_s <= lo.
+  int sa = 0, sb = a.S;
+  while (sb - sa > 1) {
+    const int mid = (sa + sb) >> 1;
+    if ((long long)Hkv * uniform(pref[mid]) <= lo) sa = mid;
+    else sb = mid;
+  }
+  struct Cursor {
+    int s, g, j, n, L;
+  };
+  auto chunks_of = [&](int s) { return uniform(pref[s + 1]) - uniform(pref[s]); };
+  Cursor ic;
+  ic.s = sa;
+  ic.n = chunks_of(sa);
+  ic.L = uniform(slen[sa]);
+  {
+    const long long rel = lo - (long long)Hkv * uniform(pref[sa]);
+    ic.g = (int)(rel / ic.n);
+    ic.j = (int)(rel - (long long)ic.g * ic.n);
+  }
+  auto advance = [&](Cursor& c) {
+    if (++c.j < c.n) return;
+    c.j = 0;
+    if (++c.g < Hkv) return;
+    c.g = 0;
+    do {
+      ++c.s;
+    } while (c.s < a.S && chunks_of(c.s) == 0);
+    if (c.s < a.S) {
+      c.n = chunks_of(c.s);
+      c.L = uniform(slen[c.s]);
+    }
+  };
+  Cursor cc = ic;
+
+  const uint32_t rs = (uint32_t)Hkv * ROW;  // bytes between slots of one head
+  const char* kpool = static_cast<const char*>(a.k);
+  const char* vpool = static_cast<const char*>(a.v);
+  Core core;
+  core.init(lane, rs);
+
+  // Block-table window of the issue cursor's sequence.
+  int tw_s = -1, tw_base = 0, tbl = 0;
+  bool tw_bad = false;
+  auto issue = [&](const Cursor& c, typename Core::Buf& b, bool& bbad) {
+    const int cs = c.j * kChunk;
+    const int bi = cs / B;
+    if (c.s != tw_s || bi < tw_base || bi >= tw_base + 64) {
+      tw_s = c.s;
+      tw_base = bi & ~63;
+      tw_bad = false;
+      const int n_blk = (c.L + B - 1) / B;
+      tbl = load_table_window(a.tables + (size_t)c.s * a.MB, tw_base, n_blk, lane, a.NB, &tw_bad);
+    }
+    bbad = tw_bad;
+    const int phys = __builtin_amdgcn_readlane(tbl, bi - tw_base);
+    const size_t cbase = ((size_t)phys * B + (size_t)(cs % B)) * rs + (size_t)c.g * ROW;
+    core.issue(kpool + cbase, vpool + cbase, rs, min(kChunk - 1, c.L - 1 - cs), b);
+  };
+
+  long long to_issue = hi - lo, to_consume = hi - lo;
+  typename Core::Buf b0, b1;
+  bool bad0 = false, bad1 = false;
+  issue(ic, b0, bad0);
+  --to_issue;
+  if (to_issue > 0) advance(ic);
+  core.fetch_q(a, cc.s, cc.g, false);
+  core.reset();
+  bool started = (cc.j == 0);
+  bool seg_bad = false;
+
+  // One chunk: issue the next one, consume the current one, close the
+  // segment piece if it ends here, step the consume cursor.
+  auto step = [&](typename Core::Buf& cur, bool curbad, typename Core::Buf& nxt, bool& nxtbad) {
+    if (to_issue > 0) {
+      issue(ic, nxt, nxtbad);
+      if (ic.j == 0) core.fetch_q(a, ic.s, ic.g, true);
+      --to_issue;
+      if (to_issue > 0) advance(ic);
+    }
+    core.consume(min(kChunk - 1, cc.L - 1 - cc.j * kChunk), a.scale_log2, cur);
+    seg_bad |= curbad;
+    --to_consume;
+    const bool seg_end = (cc.j == cc.n - 1);
+    if (seg_end || to_consume == 0) {
+      PieceSink o;
+      o.direct = started && seg_end;
+      o.bad = seg_bad;
+      o.out = a.out + ((size_t)cc.s * a.Hq + (size_t)cc.g * G) * D;
+      const size_t r0 = ((size_t)w * 2 + (started ? 1 : 0)) * G;
+      o.acc = a.ws_acc + r0 * D;
+      o.acc_stride = 1;
+      o.ml = a.ws_ml + r0;
+      o.ml_stride = 1;
+      core.finish(o);
+    }
+    if (to_consume > 0) {
+      advance(cc);
+      if (cc.j == 0) {
+        core.take_next_q();
+        core.reset();
+        started = true;
+        seg_bad = false;
+      }
+    }
+  };
+
+  while (true) {
+    step(b0, bad0, b1, bad1);
+    if (to_consume == 0) break;
+    step(b1, bad1, b0, bad0);
+    if (to_consume == 0) break;
+  }
+}
+
+// Stage 2 of the balanced schedule: one wave per query-head row (s, h), h in
+// the group of kv head g, four rows per workgroup.  An invalid length gives a
+// NaN row and L = 0 zeros; a segment that one wave finished was written by
+// stage 1; otherwise the pieces of waves w0 .. w1 (slot 1 of w0, slot 0 of
+// the later ones) are merged in wave order: exp2(m_w - M) * (acc_w, l_w)
+// summed, M the largest m_w.  Lane j owns columns j*CPL .. j*CPL + CPL - 1.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(DecodeParams a) {
+  constexpr int CPL = D / 64;  // columns per lane (1 or 2)
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWavesPerWG + uniform(threadIdx.x >> 6);  // s * Hq + query head
+  if (row >= a.S * a.Hq) return;
+  const int s = row / a.Hq;
+  const int hq = row - s * a.Hq;
+  const int G = a.Hq / a.Hkv;
+  const int g = hq / G;
+  const int h = hq - g * G;
+  const int L = a.lens[s];
+  float* o = a.out + (size_t)row * D + lane * CPL;
+  if (L < 0 || L > a.max_len || L == 0) {
+    const float fill = L == 0 ? 0.0f : __builtin_nanf("");
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) o[j] = fill;
+    return;
+  }
+  const long long T = (long long)a.Hkv * a.ws_pref[a.S];
+  const long long W_eff = balanced_workers(T, a.n_units);
+  const int n = (L + kChunk - 1) / kChunk;
+  const long long base = (long long)a.Hkv * a.ws_pref[s] + (long long)g * n;
+  const long long w0 = balanced_wave_of(base, T, W_eff);
+  const long long w1 = balanced_wave_of(base + n - 1, T, W_eff);
+  if (w0 == w1) return;
+  const int k = (int)(w1 - w0 + 1);
+  auto piece_row = [&](int p) -> size_t {
+    return ((size_t)(w0 + p) * 2 + (p == 0 ? 1 : 0)) * G + h;
+  };
+
+  float M = kNegBig;
+  for (int p = lane; p < k; p += 64) M = fmaxf(M, a.ws_ml[piece_row(p)].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  float num[CPL], den = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) num[j] = 0.0f;
+  // eight pieces per step, so eight loads are in flight at once
+  for (int p0 = 0; p0 < k; p0 += 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = p0 + i;
+      if (p < k) {
+        const size_t r = piece_row(p);
+        const float2 t = a.ws_ml[r];
+        const float f = fast_exp2(t.x - M);
+        den = fmaf(t.y, f, den);
+        if constexpr (CPL == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(a.ws_acc + r * D + lane * CPL);
+          num[0] = fmaf(x.x, f, num[0]);
+          num[1] = fmaf(x.y, f, num[1]);
+        } else {
+          num[0] = fmaf(a.ws_acc[r * D + lane], f, num[0]);
+        }
+      }
+    }
+  }
   if constexpr (CPL == 2) {
     *reinterpret_cast<float2*>(o) = make_float2(num[0] / den, num[1] / den);
   } else {
@@ -441,19 +999,124 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams a) {
   }
 }
 
-template <int DT, int D, int B>
-hipError_t launch_g(const DecodeParams& p, int group, hipStream_t stream) {
+// The same merge for long segments cut into many pieces: a workgroup of four
+// waves per query-head row.  Thread t owns column t % D and the pieces
+// w0 + t / D, w0 + t / D + SUBS, .. (SUBS = 256 / D subsets, each summed in
+// increasing order); the subsets are then added in subset order.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_reduce_balanced_wide_kernel(DecodeParams a) {
+  constexpr int SUBS = kThreads / D;
+  __shared__ float s_max[kWavesPerWG];
+  __shared__ float s_num[SUBS][D];
+  __shared__ float s_den[SUBS];
+  const int row = blockIdx.x;  // s * Hq + query head
+  const int s = row / a.Hq;
+  const int hq = row - s * a.Hq;
+  const int G = a.Hq / a.Hkv;
+  const int g = hq / G;
+  const int h = hq - g * G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int L = a.lens[s];
+  float* orow = a.out + (size_t)row * D;
+  if (L < 0 || L > a.max_len || L == 0) {
+    const float fill = L == 0 ? 0.0f : __builtin_nanf("");
+    for (int i = tid; i < D; i += kThreads) orow[i] = fill;
+    return;
+  }
+  const long long T = (long long)a.Hkv * a.ws_pref[a.S];
+  const long long W_eff = balanced_workers(T, a.n_units);
+  const int n = (L + kChunk - 1) / kChunk;
+  const long long base = (long long)a.Hkv * a.ws_pref[s] + (long long)g * n;
+  const long long w0 = balanced_wave_of(base, T, W_eff);
+  const long long w1 = balanced_wave_of(base + n - 1, T, W_eff);
+  if (w0 == w1) return;  // uniform over the workgroup
+  const int k = (int)(w1 - w0 + 1);
+  auto piece_row = [&](int p) -> size_t {
+    return ((size_t)(w0 + p) * 2 + (p == 0 ? 1 : 0)) * G + h;
+  };
+
+  float M = kNegBig;
+  for (int p = tid; p < k; p += kThreads) M = fmaxf(M, a.ws_ml[piece_row(p)].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_max[wave] = M;
+  __syncthreads();
+  M = s_max[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerWG; ++w) M = fmaxf(M, s_max[w]);
+
+  const int d = tid % D;
+  const int sub = tid / D;
+  float num = 0.0f, den = 0.0f;
+  int p = sub;
+  for (; p + 3 * SUBS < k; p += 4 * SUBS) {  // four pieces in flight
+    float2 t[4];
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t r = piece_row(p + i * SUBS);
+      t[i] = a.ws_ml[r];
+      x[i] = a.ws_acc[r * D + d];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = fast_exp2(t[i].x - M);
+      den = fmaf(t[i].y, f, den);
+      num = fmaf(x[i], f, num);
+    }
+  }
+  for (; p < k; p += SUBS) {
+    const size_t r = piece_row(p);
+    const float2 t = a.ws_ml[r];
+    const float f = fast_exp2(t.x - M);
+    den = fmaf(t.y, f, den);
+    num = fmaf(a.ws_acc[r * D + d], f, num);
+  }
+  s_num[sub][d] = num;
+  if (d == 0) s_den[sub] = den;
+  __syncthreads();
+  if (sub != 0) return;
+  float tn = 0.0f, td = 0.0f;
+#pragma unroll
+  for (int i = 0; i < SUBS; ++i) {
+    tn += s_num[i][d];
+    td += s_den[i];
+  }
+  orow[d] = tn / td;
+}
+
+// ------------------------------------------------------------------ launch
+
+template <int DT, int D, int B, int G>
+using CoreFor = typename std::conditional<(DT == 1 && G >= kMfmaMinGroup), MfmaCore<D, B, G>,
+                                          ValuCore<DT, D, B, G>>::type;
+
+template <int DT, int D, int B, int G>
+hipError_t launch_stage1(const DecodeParams& p, hipStream_t stream) {
+  using Core = CoreFor<DT, D, B, G>;
   const dim3 grid(p.grid);
-  const dim3 block(kWavesPerWG * 64);
-  switch (group) {
-    case 1: hipLaunchKernelGGL((decode_units_kernel<DT, D, B, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_units_kernel<DT, D, B, 2>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_units_kernel<DT, D, B, 4>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((decode_units_kernel<DT, D, B, 8>), grid, block, 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((decode_units_kernel<DT, D, B, 16>), grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
+  const dim3 block(kThreads);
+  if (p.schedule == kBalanced) {
+    const size_t lds = (size_t)(2 * p.S + 1) * sizeof(int);
+    hipLaunchKernelGGL((decode_balanced_kernel<Core>), grid, block, lds, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_partitioned_kernel<Core>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
+}
+
+template <int DT, int D, int B>
+hipError_t launch_g(const DecodeParams& p, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_stage1<DT, D, B, 1>(p, stream);
+    case 2: return launch_stage1<DT, D, B, 2>(p, stream);
+    case 4: return launch_stage1<DT, D, B, 4>(p, stream);
+    case 8: return launch_stage1<DT, D, B, 8>(p, stream);
+    case 16: return launch_stage1<DT, D, B, 16>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int DT, int D>
@@ -483,12 +1146,35 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_d
                     : launch_d<0>(p, head_dim, block_size, group, stream);
 }
 
-hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if (p.S == 0 || p.NP <= 1) return hipSuccess;
+hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, int group, hipStream_t stream) {
+  if (p.S == 0) return hipSuccess;
+  (void)group;
+  if (p.schedule == kBalanced) {
+    // Segments are cut into about W / (S * Hkv) pieces when the lengths are
+    // alike; many pieces per segment get four waves per row.
+    const bool wide = (long long)p.n_units >= 8LL * p.S * p.Hkv;
+    if (wide) {
+      const dim3 grid((unsigned)p.S * (unsigned)p.Hq);
+      switch (head_dim) {
+        case 64: hipLaunchKernelGGL((decode_reduce_balanced_wide_kernel<64>), grid, dim3(kThreads), 0, stream, p); break;
+        case 128: hipLaunchKernelGGL((decode_reduce_balanced_wide_kernel<128>), grid, dim3(kThreads), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      const dim3 grid((unsigned)(((long long)p.S * p.Hq + kWavesPerWG - 1) / kWavesPerWG));
+      switch (head_dim) {
+        case 64: hipLaunchKernelGGL((decode_reduce_balanced_kernel<64>), grid, dim3(kThreads), 0, stream, p); break;
+        case 128: hipLaunchKernelGGL((decode_reduce_balanced_kernel<128>), grid, dim3(kThreads), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+      }
+    }
+    return hipGetLastError();
+  }
+  if (p.NP <= 1) return hipSuccess;
   const dim3 grid((unsigned)p.S * (unsigned)p.Hq);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((decode_reduce_kernel<64>), grid, dim3(64), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((decode_reduce_kernel<128>), grid, dim3(64), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((decode_reduce_partitioned_kernel<64>), grid, dim3(kThreads), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((decode_reduce_partitioned_kernel<128>), grid, dim3(kThreads), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

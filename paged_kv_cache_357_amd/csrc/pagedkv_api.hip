@@ -18,30 +18,36 @@ bool valid_dtype(int dtype) { return dtype == PKV_DTYPE_F32 || dtype == PKV_DTYP
 int elt_bytes(int dtype) { return dtype == PKV_DTYPE_BF16 ? 2 : 4; }
 
 struct Plan {
-  int P = 0;
-  int NP = 0;
-  int n_units = 0;
+  int schedule = pkv::kPartitioned;
+  int P = 0;             // partitioned: tokens per partition
+  int NP = 0;            // partitioned: partitions per sequence
+  int n_units = 0;       // partitioned: decode units; balanced: worker waves
   int n_wg = 0;
   int xcd_group = 0;
   int grid = 0;
   size_t acc_bytes = 0;  // workspace region of partial accumulators
   size_t ml_bytes = 0;   // workspace region of partial (max, sum) pairs
-  size_t total() const { return acc_bytes + ml_bytes; }
+  size_t pref_bytes = 0; // workspace region of per-sequence chunk prefix sums (balanced)
+  size_t total() const { return acc_bytes + ml_bytes + pref_bytes; }
 };
 
-#ifndef PKV_AUTO_PARTITION
-#define PKV_AUTO_PARTITION 512
-#endif
+// Automatic partition size of the partitioned schedule.  A batch whose
+// longest sequence fits in one partition is finished in a single pass with
+// no merge; longer ones use the balanced schedule when it applies, else
+// partitions of this size.
+constexpr int kAutoPartition = 512;
 
-// Automatic partition size.  Sequences no longer than one partition are
-// finished in a single pass; longer ones are cut into partitions of a fixed
-// size, which bounds the work of one wave (so lengths that differ by 16x still
-// spread evenly over the chip) at a merge cost of (D + 2) * 4 bytes per
-// partition and query head.
 int auto_partition(int max_len) {
-  constexpr int kDefault = PKV_AUTO_PARTITION;
-  if (max_len <= kDefault) return max_len <= pkv::kChunk ? pkv::kChunk : (max_len + 15) / 16 * 16;
-  return kDefault;
+  if (max_len <= kAutoPartition) return max_len <= pkv::kChunk ? pkv::kChunk : (max_len + 15) / 16 * 16;
+  return kAutoPartition;
+}
+
+// Consecutive logical workgroups put on one XCD, and the launched grid.
+void set_grid(long long n_wg, long long group, Plan* plan) {
+  const long long span = (long long)pkv::kXcds * group;
+  plan->n_wg = (int)n_wg;
+  plan->xcd_group = (int)group;
+  plan->grid = (int)((n_wg + span - 1) / span * span);
 }
 
 int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
@@ -53,12 +59,33 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
   if (!(group == 1 || group == 2 || group == 4 || group == 8 || group == 16)) return PKV_ERR_UNSUPPORTED;
   if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
   if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
-  int P = partition_size;
-  if (P == 0) {
-    P = auto_partition(max_context_len);
-  } else if (P < pkv::kChunk || P > pkv::kMaxPartition || P % pkv::kChunk) {
+  if (partition_size != 0 &&
+      (partition_size < pkv::kChunk || partition_size > pkv::kMaxPartition || partition_size % pkv::kChunk))
     return PKV_ERR_UNSUPPORTED;
+  if ((long long)num_seqs * q_heads > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+
+  // Balanced schedule: automatic partitioning, some sequence longer than one
+  // partition, a batch whose tables fit in LDS, and chunk counts whose
+  // products with the worker count stay within 62 bits.
+  const long long chunk_bound = (long long)num_seqs * kv_heads * ((max_context_len + pkv::kChunk - 1) / pkv::kChunk);
+  const bool spills = dtype == PKV_DTYPE_F32 && head_dim == 128 && group == 16;  // one wave per SIMD is not enough
+  if (partition_size == 0 && max_context_len > kAutoPartition && num_seqs <= pkv::kBalancedMaxSeqs &&
+      chunk_bound < (1LL << 48) && !spills) {
+    const long long waves =
+        (long long)pkv::kCUs * pkv::kSimdsPerCU * pkv::balanced_waves_per_simd(dtype, head_dim, group);
+    plan->schedule = pkv::kBalanced;
+    plan->P = 0;
+    plan->NP = 0;
+    plan->n_units = (int)waves;
+    set_grid(waves / pkv::kWavesPerWG, pkv::kBalancedXcdGroup, plan);
+    const size_t rows = (size_t)waves * 2 * group;  // two partial slots per wave, a row per query head
+    plan->acc_bytes = round_up(rows * head_dim * sizeof(float), 256);
+    plan->ml_bytes = round_up(rows * 2 * sizeof(float), 256);
+    plan->pref_bytes = round_up(((size_t)num_seqs + 1) * sizeof(int32_t), 256);
+    return PKV_OK;
   }
+
+  const int P = partition_size == 0 ? auto_partition(max_context_len) : partition_size;
   const long long np = max_context_len == 0 ? 1 : ((long long)max_context_len + P - 1) / P;
   // one wave per (partition, sequence, kv head); ids and the launch grid are int
   const long long units = np * num_seqs * kv_heads;
@@ -67,20 +94,16 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
   long long xg = (seqs_grouped * kv_heads) / pkv::kWavesPerWG;
   if (xg < 1) xg = 1;
   const long long span = (long long)pkv::kXcds * xg;
-  const long long grid = (n_wg + span - 1) / span * span;
-  if (grid > 0x7fffffffLL || (long long)num_seqs * q_heads > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  if ((n_wg + span - 1) / span * span > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  plan->schedule = pkv::kPartitioned;
   plan->P = P;
   plan->NP = (int)np;
   plan->n_units = (int)units;
-  plan->n_wg = (int)n_wg;
-  plan->xcd_group = (int)xg;
-  plan->grid = (int)grid;
+  set_grid(n_wg, xg, plan);
   if (plan->NP > 1) {
     const size_t rows = (size_t)num_seqs * q_heads * plan->NP;
     plan->acc_bytes = round_up(rows * head_dim * sizeof(float), 256);
     plan->ml_bytes = round_up(rows * 2 * sizeof(float), 256);
-  } else {
-    plan->acc_bytes = plan->ml_bytes = 0;
   }
   return PKV_OK;
 }
@@ -100,8 +123,11 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   if (plan.total() > 0 && (!workspace || workspace_bytes < plan.total())) return PKV_ERR_WORKSPACE;
   (void)elt_bytes;
   p->out = out;
-  p->ws_acc = plan.total() ? static_cast<float*>(workspace) : nullptr;
-  p->ws_ml = plan.total() ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + plan.acc_bytes) : nullptr;
+  char* ws = plan.total() ? static_cast<char*>(workspace) : nullptr;
+  p->ws_acc = ws ? reinterpret_cast<float*>(ws) : nullptr;
+  p->ws_ml = ws ? reinterpret_cast<float2*>(ws + plan.acc_bytes) : nullptr;
+  p->ws_pref = ws ? reinterpret_cast<int32_t*>(ws + plan.acc_bytes + plan.ml_bytes) : nullptr;
+  p->schedule = plan.schedule;
   p->q = q;
   p->k = k_cache;
   p->v = v_cache;
@@ -162,7 +188,7 @@ int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, 
                             partition_size, &plan);
   if (st != PKV_OK) return st;
   if (resolved_partition_size) *resolved_partition_size = plan.P;
-  if (num_partitions) *num_partitions = plan.NP;
+  if (num_partitions) *num_partitions = plan.schedule == pkv::kBalanced ? plan.n_units : plan.NP;
   return PKV_OK;
 }
 
@@ -203,7 +229,7 @@ int paged_attn_decode_reduce(float* out, const void* q, const void* k_cache, con
                                 head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
                                 partition_size, workspace, workspace_bytes, &p);
   if (st != PKV_OK) return st;
-  const hipError_t e = pkv::launch_decode_reduce(p, head_dim, static_cast<hipStream_t>(stream));
+  const hipError_t e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -219,7 +245,7 @@ int paged_attn_decode(float* out, const void* q, const void* k_cache, const void
   if (st != PKV_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads, s);
-  if (e == hipSuccess) e = pkv::launch_decode_reduce(p, head_dim, s);
+  if (e == hipSuccess) e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, s);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

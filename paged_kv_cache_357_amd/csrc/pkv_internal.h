@@ -11,32 +11,59 @@ namespace pkv {
 // partitions start at multiples of it, so a chunk never straddles two
 // physical blocks.
 constexpr int kChunk = 16;
-// Largest partition (tokens) one decode unit covers.
+// Largest partition (tokens) one decode unit of the partitioned schedule covers.
 constexpr int kMaxPartition = 8192;
-// Waves per decode workgroup.  Each wave is an independent work unit.
+// Waves per decode workgroup.  Each wave is an independent worker.
 constexpr int kWavesPerWG = 4;
+// Compute units and SIMDs of an MI355X.
+constexpr int kCUs = 256;
+constexpr int kSimdsPerCU = 4;
 // Accelerator complex dies of the MI355X; consecutive workgroup ids of a
 // launch are dealt round robin over them.
 constexpr int kXcds = 8;
-// Sequences whose tiles are kept together on one XCD (so that sequences
-// forked from one prompt, which are usually neighbours, read the shared
-// blocks through the same L2).
-#ifndef PKV_SEQ_GROUP
-#define PKV_SEQ_GROUP 4
-#endif
-constexpr int kSeqGroup = PKV_SEQ_GROUP;
+// Sequences whose tiles the partitioned schedule keeps together on one XCD.
+constexpr int kSeqGroup = 4;
+// Longest batch the balanced schedule takes (its per-sequence tables live in
+// LDS: 8 bytes per sequence).
+constexpr int kBalancedMaxSeqs = 2048;
+// Fewest chunks the balanced schedule gives one wave.
+constexpr int kBalancedMinChunks = 8;
+// Logical workgroups the balanced schedule keeps together on one XCD.
+constexpr int kBalancedXcdGroup = 8;
+
+// bf16 caches with at least this many query heads per kv head use the
+// matrix-core kernels; everything else uses the vector-ALU kernels.
+constexpr int kMfmaMinGroup = 4;
+
+// Resident waves per SIMD each balanced-schedule kernel is compiled for (its
+// register budget is capped accordingly); the balanced grid holds exactly
+// that many waves on every SIMD of the chip, so all of them run at once.
+constexpr __host__ __device__ int balanced_waves_per_simd(int dtype, int head_dim, int group) {
+  return (dtype == 1 && group >= kMfmaMinGroup) ? 2                 // matrix-core kernel
+         : dtype == 1 ? ((head_dim == 128 && group == 2) ? 3 : 4)  // bf16, vector ALU
+         : head_dim == 64 ? (group <= 2 ? 4 : group == 4 ? 3 : group == 8 ? 2 : 1)
+                          : (group <= 4 ? 2 : 1);                   // fp32
+}
+
+enum Schedule : int32_t {
+  kPartitioned = 0,  // one wave per (partition, sequence, kv head)
+  kBalanced = 1      // equal shares of all chunks, one share per resident wave
+};
 
 struct DecodeParams {
   float* out;             // [S, Hq, D]
-  float* ws_acc;          // [S, Hq, NP, D]     (NP > 1 only)
-  float2* ws_ml;          // [S, Hq, NP] (m, l) (NP > 1 only)
+  float* ws_acc;          // partial accumulators (rows of D)
+  float2* ws_ml;          // partial (max, sum) pairs, one per accumulator row
+  int32_t* ws_pref;       // balanced: [S + 1] chunk prefix sums
   const void* q;          // [S, Hq, D]
   const void* k;          // [NB, B, Hkv, D]
   const void* v;          // [NB, B, Hkv, D]
   const int32_t* tables;  // [S, MB]
   const int32_t* lens;    // [S]
-  int32_t S, Hq, Hkv, NB, MB, max_len, P, NP;
-  int32_t n_units;        // NP * S * Hkv decode units (one wave each)
+  int32_t S, Hq, Hkv, NB, MB, max_len;
+  int32_t schedule;       // Schedule
+  int32_t P, NP;          // partitioned: partition size and count
+  int32_t n_units;        // partitioned: decode units; balanced: worker waves
   int32_t n_wg;           // workgroups holding them: ceil(n_units / kWavesPerWG)
   int32_t xcd_group;      // consecutive logical workgroups kept on one XCD (0: no remap)
   int32_t grid;           // launched workgroups (>= n_wg; the surplus exits at once)
@@ -46,7 +73,7 @@ struct DecodeParams {
 // Stage 1 / stage 2 launchers (decode.hip).  Return hipSuccess or the launch error.
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int block_size,
                                     int group, hipStream_t stream);
-hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, int group, hipStream_t stream);
 
 // Slot mapping and append launchers (append.hip).
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* tables, const int32_t* positions, int S, int MB,

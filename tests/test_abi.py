@@ -49,10 +49,21 @@ def test_plan_and_workspace(lib):
     # single partition: no workspace
     assert pk.plan(4, 4, 4, 64, 16, 40, 0) == (48, 1)
     assert pk.workspace_size(4, 4, 4, 64, 16, 40, 0) == 0
-    P, NP = pk.plan(64, 32, 32, 128, 16, 2048, 1)
-    assert P * NP >= 2048 and NP > 1
-    rows = 64 * 32 * NP
+    # longest sequence beyond one partition: balanced schedule, (0, worker waves);
+    # two partial rows per wave and query head of a group, plus the prefix table
+    P, W = pk.plan(64, 32, 32, 128, 16, 2048, 1)
+    assert P == 0 and W == 256 * 4 * 4
     ws = pk.workspace_size(64, 32, 32, 128, 16, 2048, 1)
+    assert ws >= W * 2 * (128 + 2) * 4 + 65 * 4 and ws % 256 == 0
+    P, W = pk.plan(8, 64, 8, 128, 16, 32768, 1)  # bf16 group 8: matrix-core kernel, 2 waves per SIMD
+    assert P == 0 and W == 256 * 4 * 2
+    assert pk.workspace_size(8, 64, 8, 128, 16, 32768, 1) >= W * 2 * 8 * (128 + 2) * 4
+    # batches too long for the LDS tables fall back to 512-token partitions
+    assert pk.plan(4096, 8, 8, 128, 16, 2048, 1) == (512, 4)
+    P, NP = pk.plan(64, 32, 32, 128, 16, 2048, 1, partition_size=512)
+    assert (P, NP) == (512, 4)
+    rows = 64 * 32 * NP
+    ws = pk.workspace_size(64, 32, 32, 128, 16, 2048, 1, partition_size=512)
     assert ws >= rows * (128 + 2) * 4 and ws % 256 == 0
     assert pk.plan(8, 64, 8, 128, 16, 32768, 1, partition_size=1024) == (1024, 32)
     assert pk.plan(2, 4, 4, 128, 16, 100, 1, partition_size=16) == (16, 7)
