@@ -2,7 +2,8 @@
 
 A step is the whole path over one batch: slot mapping for every sequence's
 new token, the K/V append into its block, the fused score / online-softmax /
-V pass over every sequence's physical blocks, and the partition merge.  The
+V pass over every sequence's physical blocks (stage 1), and the merge of the
+pieces of split segments (stage 2).  The
 workload is the Llama-7B-shaped decode batch (64 sequences, context lengths
 uniform in [128, 2048], 32 query / 32 kv heads, head_dim 128, bf16 K/V in
 16-token blocks dealt from a shuffled pool 1.25x the blocks in use).  Each
@@ -12,9 +13,11 @@ step appends the token at position L and attends over L + 1 tokens.
 
 prints one JSON line: KV GB/s of the whole step (logical K+V bytes read by
 the attention, sum(L+1) * 2 * kv_heads * head_dim * 2 B, per step time), the
-roofline of the dominant kernel (the partition kernel, its duration from HIP
-events recorded around it on the launch stream inside the timed region), and
-the fp64 CPU oracle timed on the host's cores over the same workload.
+roofline of the dominant kernel (stage 1, its duration from HIP events
+recorded around it on the launch stream inside the timed region; its HBM
+traffic from the committed rocprofv3 counter summary when that was taken on
+the same kernel source), and the fp64 CPU oracle timed on the host's cores
+over the same workload.
 """
 from __future__ import annotations
 
@@ -32,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "paged decode attention: KV GB/s and % of MI355X HBM peak; seq-tokens/s"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama7b_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_357_amd", "csrc", f) for f in ("decode.hip", "pkv_internal.h")]
 
 WORKLOADS = {"llama7b-decode": 2, "tiny-f32": 1, "gqa-lognormal": 3, "cow-parallel-sampling": 4,
@@ -54,6 +57,10 @@ def parse():
                     help="also time this many single decode launches after a 1 GiB cache flush each")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain copy of this size (reference kernel for byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of this "
+                         "workload's run with --copy-probe-mib into its traffic summary under profiles/")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the copy probe in those runs")
     return ap.parse_args()
 
 
@@ -66,14 +73,18 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(bytes_per_launch_algo: float, workload: str):
-    """HBM bytes per partition-kernel launch from the committed counter
-    summary, or None when it is missing, for another workload, or taken on a
-    different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"decode_stage1_{workload}_traffic.txt")
+
+
+def read_traffic(workload: str):
+    """HBM bytes per stage-1 launch from the committed counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         m = re.match(r"^\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
@@ -83,6 +94,83 @@ def read_traffic(bytes_per_launch_algo: float, workload: str):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def _counter_rows(folder, counter):
+    """(kernel name, dispatch id, value) of every rocprofv3 counter row named
+    `counter` in the CSV files under `folder`."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection*.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], r.get("Dispatch_Id", ""), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {folder}")
+    return rows
+
+
+def _per_dispatch(rows, pattern):
+    """Counter value per dispatch of the kernels whose name contains `pattern`
+    (rows of one dispatch, e.g. one per XCD, are summed)."""
+    acc = {}
+    for name, disp, val in rows:
+        if pattern in name:
+            acc[disp] = acc.get(disp, 0.0) + val
+    if not acc:
+        raise SystemExit(f"no dispatch of a kernel matching {pattern!r}")
+    return list(acc.values())
+
+
+def write_traffic(args):
+    """Traffic summary of the stage-1 kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what it reads on the plain copy probe
+    of known size run in the same process."""
+    from workloads import make_config
+    fetch_dir, write_dir = args.write_traffic
+    w = make_config(WORKLOADS[args.workload], values=False)
+    lens = (w.context_lens + 1).astype(np.int64)
+    algo = int(lens.sum()) * 2 * w.kv_heads * w.head_dim * w.elt
+    copy_kib = args.copy_mib * 1024.0
+    out = {}
+    for tag, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(folder, counter)
+        probe = _per_dispatch(rows, "probe_copy_kernel")
+        scale = copy_kib / float(np.mean(probe))
+        stage1 = [v for pat in ("decode_balanced_kernel", "decode_partitioned_kernel")
+                  for v in (_per_dispatch(rows, pat) if any(pat in r[0] for r in rows) else [])]
+        out[tag] = (float(np.mean(stage1)), scale, len(stage1))
+    fetch_b = out["fetch"][0] * out["fetch"][1] * 1024
+    write_b = out["write"][0] * out["write"][1] * 1024
+    cmd_run = ("python bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline "
+               "--copy-probe-mib {mib}").format(wl=args.workload, mib=args.copy_mib)
+    text = f"""# HBM traffic of the stage-1 decode kernel on the {w.name} step
+# ({w.num_seqs} sequences, {w.q_heads}/{w.kv_heads} heads, head_dim {w.head_dim}, {w.dtype} KV,
+# {w.block_size}-token blocks, context L+1), MI355X, rocprofv3 counter collection in two passes:
+#
+#   cd /tmp && export TMPDIR=/tmp && cd <repository root> &&
+#   timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- \
+#       {cmd_run}
+#   timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- \
+#       {cmd_run}
+#   python bench.py --workload {args.workload} --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
+#
+# Scaling: each counter is multiplied by (bytes the plain copy probe moves) / (what the counter reads
+# on it): FETCH_SIZE x {out['fetch'][1]:.4f}, WRITE_SIZE x {out['write'][1]:.4f} ({args.copy_mib} MiB copy).
+# Per stage-1 launch (mean of {out['fetch'][2]} / {out['write'][2]} dispatches): FETCH_SIZE {out['fetch'][0]:.0f} KiB,
+# WRITE_SIZE {out['write'][0]:.0f} KiB.  Algorithmic bytes per launch (sum(L+1) * 2 * Hkv * D * elt): {algo}.
+workload: {args.workload}
+kernel_sha: {kernel_sha()}
+fetch_bytes_per_launch: {fetch_b:.0f}
+write_bytes_per_launch: {write_b:.0f}
+hbm_bytes_per_launch: {fetch_b + write_b:.0f}
+fetch_over_algorithmic: {fetch_b / algo:.4f}
+"""
+    with open(traffic_file(args.workload), "w") as f:
+        f.write(text)
+    print(text)
 
 
 # ---------------------------------------------------------------- CPU leg
@@ -129,6 +217,9 @@ def cpu_baseline(w, lens, n_seqs):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (the decode shards over "
               "sequences or kv heads with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
@@ -157,6 +248,7 @@ def main():
     slots = torch.empty(w.num_seqs, dtype=torch.int32, device=dev)
     call = pk.DecodeCall(q, kc, vc, tables, lens, w.scale, max_len, args.partition_size)
     P, NP = call.plan
+    balanced = P == 0  # balanced schedule: NP is the number of worker waves
 
     def step(ev=None):
         if ev is not None:
@@ -192,7 +284,7 @@ def main():
     tokens = int(lens_step.astype(np.int64).sum())
     value = kv_bytes / (ms_step / 1e3) / 1e9
     achieved = kv_bytes / (part_ms / 1e3) / 1e9
-    traffic = read_traffic(kv_bytes, args.workload)
+    traffic = read_traffic(args.workload)
 
     extra = {
         "kv_bytes_per_step": kv_bytes,
@@ -200,6 +292,7 @@ def main():
         "seq_tokens_per_s": tokens / (ms_step / 1e3),
         "decode_tokens_per_s": w.num_seqs / (ms_step / 1e3),
         "partition_kernel_ms": part_ms, "reduce_kernel_ms": red_ms, "slot_map_append_ms": app_ms,
+        "schedule": "balanced" if balanced else "partitioned",
         "partition_size": P, "num_partitions": NP,
         "kernel_sha": kernel_sha(),
     }
@@ -286,7 +379,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "decode_partition_kernel", "algorithmic_bytes_per_launch": kv_bytes,
+            "kernel": "decode_balanced_kernel" if balanced else "decode_partitioned_kernel",
+            "algorithmic_bytes_per_launch": kv_bytes,
         },
         "cpu_baseline": cpu,
         "extra": extra,

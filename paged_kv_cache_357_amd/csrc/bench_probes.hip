@@ -18,13 +18,25 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(uint4* __restrict_
   for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) dst[i] = src[i];
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming read: each thread keeps eight 16-byte nontemporal loads in
+// flight per step (the access pattern the decode's K/V reads aim for).
 __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint4* __restrict__ src, size_t n,
                                                              uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * kThreads;
+  constexpr int U = 8;
+  const size_t tile = (size_t)kThreads * U;
+  const u32x4* p = reinterpret_cast<const u32x4*>(src);
   uint32_t acc = 0;
-  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
-    const uint4 v = src[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  for (size_t base = (size_t)blockIdx.x * tile; base < n; base += (size_t)gridDim.x * tile) {
+    u32x4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const size_t i = base + (size_t)j * kThreads + threadIdx.x;
+      v[j] = i < n ? __builtin_nontemporal_load(p + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
   // keeps the loads alive; the condition practically never holds
   if (acc == 0x9E3779B9u) sink[0] = acc;
@@ -38,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void probe_fill_kernel(uint4* __restrict_
 
 unsigned grid_for(size_t n) {
   const size_t want = (n + kThreads - 1) / kThreads;
-  const size_t cap = 256 * 16;  // 16 workgroups per CU on 256 CUs
+  const size_t cap = 256 * 32;  // 32 workgroups per CU on 256 CUs
   return (unsigned)(want < cap ? (want ? want : 1) : cap);
 }
 
