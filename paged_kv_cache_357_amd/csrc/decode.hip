@@ -81,7 +81,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Cache-policy operand of the buffer loads: bit 1 is the nontemporal hint.
+// Cache-policy operand of the K / V buffer loads: bit 1 is the nontemporal
+// hint (the rows are streamed once per call).
 constexpr int kStreamPolicy = PKV_NT_LOADS ? 2 : 0;
 // Fourth word of a raw buffer resource on gfx9-family parts (gfx950).
 constexpr int kBufferConfig = 0x00020000;
@@ -106,16 +107,6 @@ __device__ __forceinline__ u32x2 make_u32x2(uint32_t x, uint32_t y) { return u32
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
-}
-
-// One 16-byte column of a K or V row.  The rows are streamed once per call,
-// so they are fetched with the nontemporal hint.
-__device__ __forceinline__ u32x4 load_row16(const char* p) {
-#if PKV_NT_LOADS
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
-  return *reinterpret_cast<const u32x4*>(p);
-#endif
 }
 
 template <int CTRL>
@@ -187,18 +178,24 @@ struct ValuCore {
   static constexpr int kHeadDim = D;
   static constexpr int kGroup = G;
   static constexpr int kWavesPerSimd = balanced_waves_per_simd(DT, D, G);
+  static constexpr int kPipeline = balanced_pipeline_depth(DT, D, G);
   static_assert(LPT == 8 || LPT == 16 || LPT == 32, "row must span 8, 16 or 32 lanes");
   static_assert(B % kChunk == 0, "block size must be a multiple of the chunk");
 
+  // One chunk in flight: its K and V columns and, when the chunk opens a
+  // segment, that segment's query columns.
   struct Buf {
     u32x4 k[NI], v[NI];
+    uint32_t q[G][4];
   };
 
   int grp, seg;
-  uint32_t q[G][4], qn[G][4];
+  uint32_t q[G][4];
   float m[G], l[G], acc[G][EPL];
 
-  __device__ void init(int lane, uint32_t /*rs*/) {
+  static constexpr int kStageBytes = 16;  // no LDS tile
+
+  __device__ void init(int lane, uint32_t /*rs*/, char* /*stage_tile*/) {
     grp = lane / LPT;
     seg = lane % LPT;
   }
@@ -214,36 +211,41 @@ struct ValuCore {
   }
 
   // Query rows of heads g*G .. g*G+G-1 of sequence s: this lane's column.
-  __device__ void fetch_q(const DecodeParams& a, int s, int g, bool into_next) {
+  __device__ void fetch_q(const DecodeParams& a, int s, int g, uint32_t (&dst)[G][4]) const {
     const char* qsrc = static_cast<const char*>(a.q) + ((size_t)s * a.Hq + (size_t)g * G) * ROW + seg * 16;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const uint4 t = *reinterpret_cast<const uint4*>(qsrc + h * ROW);
-      uint32_t* d = into_next ? qn[h] : q[h];
-      d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
+      dst[h][0] = t.x; dst[h][1] = t.y; dst[h][2] = t.z; dst[h][3] = t.w;
     }
   }
+  __device__ void load_q(const DecodeParams& a, int s, int g) { fetch_q(a, s, g, q); }
+  __device__ void fetch_q(const DecodeParams& a, int s, int g, Buf& b) const { fetch_q(a, s, g, b.q); }
 
-  __device__ void take_next_q() {
+  __device__ void take_q(const Buf& b) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[h][i] = qn[h][i];
+      for (int i = 0; i < 4; ++i) q[h][i] = b.q[h][i];
   }
 
   // Loads of one chunk: kc / vc point at the chunk's first row of this kv
-  // head; rows past `lim` repeat row `lim`.
-  __device__ void issue(const char* kc, const char* vc, uint32_t rs, int lim, Buf& b) const {
+  // head; the buffer resources cover `nbytes` from there (rows 0 .. lim, or
+  // nothing for a load-free dummy), so rows past the end read as zero.
+  __device__ void issue(const char* kc, const char* vc, uint32_t rs, uint32_t nbytes, Buf& b) const {
+    const __amdgpu_buffer_rsrc_t kres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kc), 0, (int)nbytes, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t vres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vc), 0, (int)nbytes, kBufferConfig);
+    const uint32_t off = (uint32_t)grp * rs + (uint32_t)seg * 16;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const uint32_t t = (uint32_t)min(i * TPI + grp, lim);
-      b.k[i] = load_row16(kc + t * rs + seg * 16);
-    }
+    for (int i = 0; i < NI; ++i)
+      b.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, (int)(off + (uint32_t)(i * TPI) * rs),
+                                                                               0, kStreamPolicy));
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const uint32_t t = (uint32_t)min(i * TPI + grp, lim);
-      b.v[i] = load_row16(vc + t * rs + seg * 16);
-    }
+    for (int i = 0; i < NI; ++i)
+      b.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)(off + (uint32_t)(i * TPI) * rs),
+                                                                               0, kStreamPolicy));
   }
 
   // Partial dot product of this lane's 16-byte column of q and of a K row.
@@ -402,26 +404,41 @@ struct MfmaCore {
   static constexpr int kHeadDim = D;
   static constexpr int kGroup = G;
   static constexpr int kWavesPerSimd = balanced_waves_per_simd(1, D, G);
+  static constexpr int kPipeline = balanced_pipeline_depth(1, D, G);
   static_assert(G <= 16, "a group must fit the 16 columns of a tile");
   static_assert(B % kChunk == 0, "block size must be a multiple of the chunk");
   using VRow = typename std::conditional<CW == 8, u32x4, u32x2>::type;
+  // K rows are loaded whole (LPR lanes of 16 bytes per row, RPI rows per
+  // instruction), staged in a per-wave LDS tile and read back in operand
+  // layout.  Tile position of 16-byte column c of row r: c ^ (r mod LPR),
+  // so that both the row-wise writes and the operand reads (16 rows at one
+  // column) spread over distinct banks.
+  static constexpr int LPR = ROW / 16;
+  static constexpr int RPI = 64 / LPR;
+  static constexpr int NK = kChunk / RPI;
+  static constexpr int kStageBytes = kChunk * ROW;
 
+  // One chunk in flight: its K rows, V operands and, when the chunk opens a
+  // segment, that segment's q^T operand.
   struct Buf {
-    u32x4 k[KSTEPS];
+    u32x4 k[NK];
     VRow v[4];
+    bf16x8 q[KSTEPS];
   };
 
   int gl, cl;
-  uint32_t koff, voff;
-  bf16x8 q[KSTEPS], qn[KSTEPS];
+  uint32_t kld, voff;
+  char* stage;  // this wave's LDS tile
+  bf16x8 q[KSTEPS];
   f32x4 acc[CW];
   float m_run, l_run;
 
-  __device__ void init(int lane, uint32_t rs) {
+  __device__ void init(int lane, uint32_t rs, char* stage_tile) {
     gl = lane >> 4;
     cl = lane & 15;
-    koff = (uint32_t)cl * rs + 16u * (uint32_t)gl;             // + 64 j
-    voff = (uint32_t)(4 * gl) * rs + (uint32_t)cl * (2 * CW);   // + r rs
+    kld = (uint32_t)(lane / LPR) * rs + (uint32_t)(lane % LPR) * 16;   // + RPI i rs
+    voff = (uint32_t)(4 * gl) * rs + (uint32_t)cl * (2 * CW);        // + r rs
+    stage = stage_tile;
   }
 
   __device__ void reset() {
@@ -432,32 +449,32 @@ struct MfmaCore {
   }
 
   // q^T operand: column cl is query head g*G + cl of the group.
-  __device__ void fetch_q(const DecodeParams& a, int s, int g, bool into_next) {
+  __device__ void fetch_q(const DecodeParams& a, int s, int g, bf16x8 (&dst)[KSTEPS]) const {
     const char* qsrc = static_cast<const char*>(a.q) + ((size_t)s * a.Hq + (size_t)g * G + cl) * ROW;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
       uint4 t = make_uint4(0, 0, 0, 0);
       if (cl < G) t = *reinterpret_cast<const uint4*>(qsrc + 16 * (gl + 4 * j));
-      const bf16x8 v = __builtin_bit_cast(bf16x8, make_u32x4(t));
-      if (into_next) qn[j] = v; else q[j] = v;
+      dst[j] = __builtin_bit_cast(bf16x8, make_u32x4(t));
     }
   }
+  __device__ void load_q(const DecodeParams& a, int s, int g) { fetch_q(a, s, g, q); }
+  __device__ void fetch_q(const DecodeParams& a, int s, int g, Buf& b) const { fetch_q(a, s, g, b.q); }
 
-  __device__ void take_next_q() {
+  __device__ void take_q(const Buf& b) {
 #pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) q[j] = qn[j];
+    for (int j = 0; j < KSTEPS; ++j) q[j] = b.q[j];
   }
 
-  __device__ void issue(const char* kc, const char* vc, uint32_t rs, int lim, Buf& b) const {
-    const uint32_t nbytes = (uint32_t)lim * rs + ROW;  // rows 0 .. lim of this head
+  __device__ void issue(const char* kc, const char* vc, uint32_t rs, uint32_t nbytes, Buf& b) const {
     const __amdgpu_buffer_rsrc_t kres =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kc), 0, (int)nbytes, kBufferConfig);
     const __amdgpu_buffer_rsrc_t vres =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vc), 0, (int)nbytes, kBufferConfig);
 #pragma unroll
-    for (int j = 0; j < KSTEPS; ++j)
-      b.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, (int)(koff + 64u * j), 0,
-                                                                               kStreamPolicy));
+    for (int i = 0; i < NK; ++i)
+      b.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, (int)(kld + (uint32_t)(RPI * i) * rs),
+                                                                               0, kStreamPolicy));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (CW == 8)
@@ -470,10 +487,20 @@ struct MfmaCore {
   }
 
   __device__ void consume(int lim, float sl2, const Buf& b) {
+    const int lane = gl * 16 + cl;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int r = RPI * i + lane / LPR;
+      const int c = (lane % LPR) ^ (r % LPR);
+      *reinterpret_cast<u32x4*>(stage + r * ROW + c * 16) = b.k[i];
+    }
     f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < KSTEPS; ++j)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[j]), q[j], sc, 0, 0, 0);
+    for (int j = 0; j < KSTEPS; ++j) {
+      const int c = (gl + 4 * j) ^ (cl % LPR);
+      const u32x4 k = *reinterpret_cast<const u32x4*>(stage + cl * ROW + c * 16);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), q[j], sc, 0, 0, 0);
+    }
 
     float x[4];
     float mx = m_run;
@@ -563,6 +590,7 @@ struct MfmaCore {
 template <class Core>
 __global__ __launch_bounds__(kThreads) void decode_partitioned_kernel(DecodeParams a) {
   constexpr int B = Core::kBlock, D = Core::kHeadDim, G = Core::kGroup, ROW = Core::ROW;
+  __shared__ __attribute__((aligned(16))) char s_stage[kWavesPerWG][Core::kStageBytes];
   const int ell = logical_workgroup(blockIdx.x, a.xcd_group, a.n_wg);
   if (ell < 0) return;
   const int wave = uniform(threadIdx.x >> 6);
@@ -601,11 +629,11 @@ __global__ __launch_bounds__(kThreads) void decode_partitioned_kernel(DecodePara
   const char* vbase = static_cast<const char*>(a.v) + (size_t)g * ROW;
 
   Core core;
-  core.init(lane, rs);
+  core.init(lane, rs, s_stage[wave]);
   bool bad = false;
   int wbase = 0;
   int tbl = load_table_window(trow, 0, n_blk, lane, a.NB, &bad);
-  core.fetch_q(a, s, g, false);
+  core.load_q(a, s, g);
   core.reset();
 
   auto issue = [&](int c, typename Core::Buf& b) {
@@ -617,18 +645,31 @@ __global__ __launch_bounds__(kThreads) void decode_partitioned_kernel(DecodePara
     }
     const int phys = __builtin_amdgcn_readlane(tbl, bi - wbase);
     const size_t cbase = ((size_t)phys * B + (size_t)(cs % B)) * rs;
-    core.issue(kbase + cbase, vbase + cbase, rs, tok_end - 1 - cs, b);
+    const int lim = min(kChunk - 1, tok_end - 1 - cs);  // last valid row of the chunk
+    core.issue(kbase + cbase, vbase + cbase, rs, (uint32_t)lim * rs + ROW, b);
   };
 
+  // The loads of chunk c+1 are issued before chunk c is consumed.  The steady
+  // state issues unconditionally (the last one or two chunks are peeled), so
+  // the wait before each consume covers only the older chunk's loads.
+  auto consume = [&](int c, const typename Core::Buf& b) {
+    core.consume(tok_end - 1 - (tok0 + c * kChunk), a.scale_log2, b);
+  };
   typename Core::Buf ba, bb;
   issue(0, ba);
-  for (int c = 0; c < n_chunks; c += 2) {
-    if (c + 1 < n_chunks) issue(c + 1, bb);
-    core.consume(tok_end - 1 - (tok0 + c * kChunk), a.scale_log2, ba);
-    if (c + 1 < n_chunks) {
-      if (c + 2 < n_chunks) issue(c + 2, ba);
-      core.consume(tok_end - 1 - (tok0 + (c + 1) * kChunk), a.scale_log2, bb);
-    }
+  int c = 0;
+  for (; c + 2 < n_chunks; c += 2) {
+    issue(c + 1, bb);
+    consume(c, ba);
+    issue(c + 2, ba);
+    consume(c + 1, bb);
+  }
+  if (c + 1 < n_chunks) {
+    issue(c + 1, bb);
+    consume(c, ba);
+    consume(c + 1, bb);
+  } else {
+    consume(c, ba);
   }
 
   PieceSink o;
@@ -762,6 +803,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Core::
 void decode_balanced_kernel(DecodeParams a) {
   constexpr int B = Core::kBlock, D = Core::kHeadDim, G = Core::kGroup, ROW = Core::ROW;
   extern __shared__ int smem[];
+  __shared__ __attribute__((aligned(16))) char s_stage[kWavesPerWG][Core::kStageBytes];
   int* pref = smem;               // [S + 1] chunk prefix sums C_s
   int* slen = smem + a.S + 1;     // [S] lengths (0 for invalid ones)
   __shared__ int s_wave_sum[kWavesPerWG];
@@ -802,25 +844,33 @@ void decode_balanced_kernel(DecodeParams a) {
   if (blockIdx.x == 0)
     for (int s = tid; s <= a.S; s += kThreads) a.ws_pref[s] = pref[s];
 
+  // Work is laid out over (sequence, head group, chunk); a head group is HG
+  // adjacent kv heads.  With HG = 1 each wave is a worker; with HG = 4 the
+  // four waves of a workgroup share one share and take one head of the group
+  // each, so they read adjacent 256-byte rows of the same tokens together.
   const int Hkv = a.Hkv;
-  const long long T = (long long)Hkv * uniform(pref[a.S]);
+  const int HG = a.head_group;
+  const int NGR = Hkv / HG;
+  const long long T = (long long)NGR * uniform(pref[a.S]);
   const int ell = logical_workgroup(blockIdx.x, a.xcd_group, a.n_wg);
   if (ell < 0 || T == 0) return;
-  const long long W_eff = balanced_workers(T, a.n_units);
-  const int w = ell * kWavesPerWG + wave;
-  if (w >= W_eff) return;
-  const long long lo = (long long)w * T / W_eff;
-  const long long hi = (long long)(w + 1) * T / W_eff;
+  const int w = ell * kWavesPerWG + wave;               // this wave's partial-record slots
+  const int worker = HG == 1 ? w : ell;
+  const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
+  if (worker >= W_eff) return;
+  const int hsub = HG == 1 ? 0 : wave;                  // head of the group this wave takes
+  const long long lo = (long long)worker * T / W_eff;
+  const long long hi = (long long)(worker + 1) * T / W_eff;
 
-  // Locate the segment holding chunk lo: the last s with Hkv * C_s <= lo.
+  // Locate the segment holding chunk lo: the last s with NGR * C_s <= lo.
   int sa = 0, sb = a.S;
   while (sb - sa > 1) {
     const int mid = (sa + sb) >> 1;
-    if ((long long)Hkv * uniform(pref[mid]) <= lo) sa = mid;
+    if ((long long)NGR * uniform(pref[mid]) <= lo) sa = mid;
     else sb = mid;
   }
   struct Cursor {
-    int s, g, j, n, L;
+    int s, g, j, n, L;  // g: head group
   };
   auto chunks_of = [&](int s) { return uniform(pref[s + 1]) - uniform(pref[s]); };
   Cursor ic;
@@ -828,14 +878,14 @@ void decode_balanced_kernel(DecodeParams a) {
   ic.n = chunks_of(sa);
   ic.L = uniform(slen[sa]);
   {
-    const long long rel = lo - (long long)Hkv * uniform(pref[sa]);
+    const long long rel = lo - (long long)NGR * uniform(pref[sa]);
     ic.g = (int)(rel / ic.n);
     ic.j = (int)(rel - (long long)ic.g * ic.n);
   }
   auto advance = [&](Cursor& c) {
     if (++c.j < c.n) return;
     c.j = 0;
-    if (++c.g < Hkv) return;
+    if (++c.g < NGR) return;
     c.g = 0;
     do {
       ++c.s;
@@ -851,46 +901,67 @@ void decode_balanced_kernel(DecodeParams a) {
   const char* kpool = static_cast<const char*>(a.k);
   const char* vpool = static_cast<const char*>(a.v);
   Core core;
-  core.init(lane, rs);
+  core.init(lane, rs, s_stage[wave]);
 
   // Block-table window of the issue cursor's sequence.
   int tw_s = -1, tw_base = 0, tbl = 0;
   bool tw_bad = false;
-  auto issue = [&](const Cursor& c, typename Core::Buf& b, bool& bbad) {
-    const int cs = c.j * kChunk;
-    const int bi = cs / B;
-    if (c.s != tw_s || bi < tw_base || bi >= tw_base + 64) {
-      tw_s = c.s;
-      tw_base = bi & ~63;
-      tw_bad = false;
-      const int n_blk = (c.L + B - 1) / B;
-      tbl = load_table_window(a.tables + (size_t)c.s * a.MB, tw_base, n_blk, lane, a.NB, &tw_bad);
-    }
-    bbad = tw_bad;
-    const int phys = __builtin_amdgcn_readlane(tbl, bi - tw_base);
-    const size_t cbase = ((size_t)phys * B + (size_t)(cs % B)) * rs + (size_t)c.g * ROW;
-    core.issue(kpool + cbase, vpool + cbase, rs, min(kChunk - 1, c.L - 1 - cs), b);
-  };
 
+  // Software pipeline of depth NB: the loads of the next NB-1 chunks are in
+  // flight while a chunk is consumed.  Every step issues the same load
+  // sequence: the next chunk of the share, or past its end a load-free dummy
+  // (zero-size resources), so the wait before each consume covers only the
+  // consumed chunk's loads.  A chunk that opens a segment (or the wave's
+  // first chunk) also brings the segment's query rows, loaded before the
+  // chunk's rows.
+  constexpr int NB = Core::kPipeline;
   long long to_issue = hi - lo, to_consume = hi - lo;
-  typename Core::Buf b0, b1;
-  bool bad0 = false, bad1 = false;
-  issue(ic, b0, bad0);
-  --to_issue;
-  if (to_issue > 0) advance(ic);
-  core.fetch_q(a, cc.s, cc.g, false);
-  core.reset();
-  bool started = (cc.j == 0);
-  bool seg_bad = false;
-
-  // One chunk: issue the next one, consume the current one, close the
-  // segment piece if it ends here, step the consume cursor.
-  auto step = [&](typename Core::Buf& cur, bool curbad, typename Core::Buf& nxt, bool& nxtbad) {
+  typename Core::Buf buf[NB];
+  bool bad[NB];
+  bool first_issue = true;
+  auto issue_next = [&](typename Core::Buf& b, bool& bbad) {
+    const char* kc = kpool;
+    const char* vc = vpool;
+    uint32_t nbytes = 0;
+    bbad = false;
     if (to_issue > 0) {
-      issue(ic, nxt, nxtbad);
-      if (ic.j == 0) core.fetch_q(a, ic.s, ic.g, true);
+      if (first_issue || ic.j == 0) core.fetch_q(a, ic.s, ic.g * HG + hsub, b);
+      first_issue = false;
+      const int cs = ic.j * kChunk;
+      const int bi = cs / B;
+      if (ic.s != tw_s || bi < tw_base || bi >= tw_base + 64) {
+        tw_s = ic.s;
+        tw_base = bi & ~63;
+        tw_bad = false;
+        const int n_blk = (ic.L + B - 1) / B;
+        tbl = load_table_window(a.tables + (size_t)ic.s * a.MB, tw_base, n_blk, lane, a.NB, &tw_bad);
+      }
+      bbad = tw_bad;
+      const int phys = __builtin_amdgcn_readlane(tbl, bi - tw_base);
+      const size_t cbase = ((size_t)phys * B + (size_t)(cs % B)) * rs + (size_t)(ic.g * HG + hsub) * ROW;
+      kc = kpool + cbase;
+      vc = vpool + cbase;
+      nbytes = (uint32_t)min(kChunk - 1, ic.L - 1 - cs) * rs + ROW;  // rows 0 .. lim of this head
       --to_issue;
       if (to_issue > 0) advance(ic);
+    }
+    core.issue(kc, vc, rs, nbytes, b);
+  };
+
+  bool started = false;
+  bool seg_bad = false;
+  bool first_consume = true;
+  // One step: issue into the slot consumed one step earlier, consume the
+  // current chunk, close the segment piece if it ends here, step the cursor.
+  auto step = [&](typename Core::Buf& cur, bool curbad, typename Core::Buf& nxt, bool& nxtbad) {
+    issue_next(nxt, nxtbad);
+    if (to_consume <= 0) return;
+    if (first_consume || cc.j == 0) {
+      core.take_q(cur);
+      core.reset();
+      started = (cc.j == 0);
+      seg_bad = false;
+      first_consume = false;
     }
     core.consume(min(kChunk - 1, cc.L - 1 - cc.j * kChunk), a.scale_log2, cur);
     seg_bad |= curbad;
@@ -900,7 +971,7 @@ void decode_balanced_kernel(DecodeParams a) {
       PieceSink o;
       o.direct = started && seg_end;
       o.bad = seg_bad;
-      o.out = a.out + ((size_t)cc.s * a.Hq + (size_t)cc.g * G) * D;
+      o.out = a.out + ((size_t)cc.s * a.Hq + (size_t)(cc.g * HG + hsub) * G) * D;
       const size_t r0 = ((size_t)w * 2 + (started ? 1 : 0)) * G;
       o.acc = a.ws_acc + r0 * D;
       o.acc_stride = 1;
@@ -908,22 +979,14 @@ void decode_balanced_kernel(DecodeParams a) {
       o.ml_stride = 1;
       core.finish(o);
     }
-    if (to_consume > 0) {
-      advance(cc);
-      if (cc.j == 0) {
-        core.take_next_q();
-        core.reset();
-        started = true;
-        seg_bad = false;
-      }
-    }
+    if (to_consume > 0) advance(cc);
   };
 
-  while (true) {
-    step(b0, bad0, b1, bad1);
-    if (to_consume == 0) break;
-    step(b1, bad1, b0, bad0);
-    if (to_consume == 0) break;
+#pragma unroll
+  for (int k = 0; k < NB - 1; ++k) issue_next(buf[k], bad[k]);
+  while (to_consume > 0) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) step(buf[k], bad[k], buf[(k + NB - 1) % NB], bad[(k + NB - 1) % NB]);
   }
 }
 
@@ -952,16 +1015,20 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(Decode
     for (int j = 0; j < CPL; ++j) o[j] = fill;
     return;
   }
-  const long long T = (long long)a.Hkv * a.ws_pref[a.S];
-  const long long W_eff = balanced_workers(T, a.n_units);
+  const int HG = a.head_group;
+  const int NGR = a.Hkv / HG;
+  const long long T = (long long)NGR * a.ws_pref[a.S];
+  const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
   const int n = (L + kChunk - 1) / kChunk;
-  const long long base = (long long)a.Hkv * a.ws_pref[s] + (long long)g * n;
-  const long long w0 = balanced_wave_of(base, T, W_eff);
+  const long long base = (long long)NGR * a.ws_pref[s] + (long long)(g / HG) * n;
+  const long long w0 = balanced_wave_of(base, T, W_eff);  // first and last worker of the segment
   const long long w1 = balanced_wave_of(base + n - 1, T, W_eff);
+  const int hsub = g % HG;
   if (w0 == w1) return;
   const int k = (int)(w1 - w0 + 1);
   auto piece_row = [&](int p) -> size_t {
-    return ((size_t)(w0 + p) * 2 + (p == 0 ? 1 : 0)) * G + h;
+    const size_t wave_id = HG == 1 ? (size_t)(w0 + p) : (size_t)(w0 + p) * kWavesPerWG + hsub;
+    return (wave_id * 2 + (p == 0 ? 1 : 0)) * G + h;
   };
 
   float M = kNegBig;
@@ -1025,16 +1092,20 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_wide_kernel(D
     for (int i = tid; i < D; i += kThreads) orow[i] = fill;
     return;
   }
-  const long long T = (long long)a.Hkv * a.ws_pref[a.S];
-  const long long W_eff = balanced_workers(T, a.n_units);
+  const int HG = a.head_group;
+  const int NGR = a.Hkv / HG;
+  const long long T = (long long)NGR * a.ws_pref[a.S];
+  const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
   const int n = (L + kChunk - 1) / kChunk;
-  const long long base = (long long)a.Hkv * a.ws_pref[s] + (long long)g * n;
-  const long long w0 = balanced_wave_of(base, T, W_eff);
+  const long long base = (long long)NGR * a.ws_pref[s] + (long long)(g / HG) * n;
+  const long long w0 = balanced_wave_of(base, T, W_eff);  // first and last worker of the segment
   const long long w1 = balanced_wave_of(base + n - 1, T, W_eff);
+  const int hsub = g % HG;
   if (w0 == w1) return;  // uniform over the workgroup
   const int k = (int)(w1 - w0 + 1);
   auto piece_row = [&](int p) -> size_t {
-    return ((size_t)(w0 + p) * 2 + (p == 0 ? 1 : 0)) * G + h;
+    const size_t wave_id = HG == 1 ? (size_t)(w0 + p) : (size_t)(w0 + p) * kWavesPerWG + hsub;
+    return (wave_id * 2 + (p == 0 ? 1 : 0)) * G + h;
   };
 
   float M = kNegBig;

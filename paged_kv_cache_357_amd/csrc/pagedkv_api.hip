@@ -24,6 +24,7 @@ struct Plan {
   int n_units = 0;       // partitioned: decode units; balanced: worker waves
   int n_wg = 0;
   int xcd_group = 0;
+  int head_group = 1;
   int grid = 0;
   size_t acc_bytes = 0;  // workspace region of partial accumulators
   size_t ml_bytes = 0;   // workspace region of partial (max, sum) pairs
@@ -76,6 +77,8 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
     plan->schedule = pkv::kBalanced;
     plan->P = 0;
     plan->NP = 0;
+    // matrix-core kernels: four waves of a workgroup on four adjacent heads
+    plan->head_group = (dtype == PKV_DTYPE_BF16 && group >= pkv::kMfmaMinGroup && kv_heads % 4 == 0) ? 4 : 1;
     plan->n_units = (int)waves;
     set_grid(waves / pkv::kWavesPerWG, pkv::kBalancedXcdGroup, plan);
     const size_t rows = (size_t)waves * 2 * group;  // two partial slots per wave, a row per query head
@@ -144,6 +147,7 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   p->n_units = plan.n_units;
   p->n_wg = plan.n_wg;
   p->xcd_group = plan.xcd_group;
+  p->head_group = plan.head_group;
   p->grid = plan.grid;
   p->scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   return PKV_OK;

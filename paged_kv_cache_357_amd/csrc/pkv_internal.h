@@ -38,11 +38,20 @@ constexpr int kMfmaMinGroup = 4;
 // Resident waves per SIMD each balanced-schedule kernel is compiled for (its
 // register budget is capped accordingly); the balanced grid holds exactly
 // that many waves on every SIMD of the chip, so all of them run at once.
+// Fewer, deeper streams read the paged pool faster than many shallow ones.
+#ifndef PKV_BALANCED_WAVES
+#define PKV_BALANCED_WAVES 1
+#endif
+#ifndef PKV_PIPELINE
+#define PKV_PIPELINE 3
+#endif
 constexpr __host__ __device__ int balanced_waves_per_simd(int dtype, int head_dim, int group) {
-  return (dtype == 1 && group >= kMfmaMinGroup) ? 2                 // matrix-core kernel
-         : dtype == 1 ? ((head_dim == 128 && group == 2) ? 3 : 4)  // bf16, vector ALU
-         : head_dim == 64 ? (group <= 2 ? 4 : group == 4 ? 3 : group == 8 ? 2 : 1)
-                          : (group <= 4 ? 2 : 1);                   // fp32
+  return (dtype == 0 && (group >= 4 || (head_dim == 128 && group >= 2))) ? 1 : PKV_BALANCED_WAVES;
+}
+// Chunks in flight per wave in the balanced schedule (registers of the
+// fp32 kernels with wide groups allow only two).
+constexpr __host__ __device__ int balanced_pipeline_depth(int dtype, int head_dim, int group) {
+  return (dtype == 0 && (group >= 4 || (head_dim == 128 && group >= 2))) ? 2 : PKV_PIPELINE;
 }
 
 enum Schedule : int32_t {
@@ -66,6 +75,7 @@ struct DecodeParams {
   int32_t n_units;        // partitioned: decode units; balanced: worker waves
   int32_t n_wg;           // workgroups holding them: ceil(n_units / kWavesPerWG)
   int32_t xcd_group;      // consecutive logical workgroups kept on one XCD (0: no remap)
+  int32_t head_group;     // balanced: adjacent kv heads the waves of a workgroup take in lockstep (1 or 4)
   int32_t grid;           // launched workgroups (>= n_wg; the surplus exits at once)
   float scale_log2;       // scale * log2(e): scores live in the base-2 domain
 };
