@@ -52,11 +52,11 @@ def test_plan_and_workspace(lib):
     # longest sequence beyond one partition: balanced schedule, (0, worker waves);
     # two partial rows per wave and query head of a group, plus the prefix table
     P, W = pk.plan(64, 32, 32, 128, 16, 2048, 1)
-    assert P == 0 and W == 256 * 4 * 4
+    assert P == 0 and W == 256 * 4  # one worker wave per SIMD of 256 CUs
     ws = pk.workspace_size(64, 32, 32, 128, 16, 2048, 1)
     assert ws >= W * 2 * (128 + 2) * 4 + 65 * 4 and ws % 256 == 0
-    P, W = pk.plan(8, 64, 8, 128, 16, 32768, 1)  # bf16 group 8: matrix-core kernel, 2 waves per SIMD
-    assert P == 0 and W == 256 * 4 * 2
+    P, W = pk.plan(8, 64, 8, 128, 16, 32768, 1)  # bf16 group 8: matrix-core kernel
+    assert P == 0 and W == 256 * 4
     assert pk.workspace_size(8, 64, 8, 128, 16, 32768, 1) >= W * 2 * 8 * (128 + 2) * 4
     # batches too long for the LDS tables fall back to 512-token partitions
     assert pk.plan(4096, 8, 8, 128, 16, 2048, 1) == (512, 4)
