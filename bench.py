@@ -1,7 +1,7 @@
 """Benchmark: one decode step of paged attention on one MI355X.
 
 A step is the whole path over one batch: slot mapping for every sequence's
-new token, the K/V append into its block, the fused score / online-softmax /
+new token and the K/V append into its block (one launch), the fused score / online-softmax /
 V pass over every sequence's physical blocks (stage 1), and the merge of the
 pieces of split segments (stage 2).  The
 workload is the Llama-7B-shaped decode batch (64 sequences, context lengths
@@ -253,8 +253,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        pk.slot_mapping(tables, pos, w.num_blocks, w.block_size, out=slots)
-        pk.append(kc, vc, kn, vn, slots)
+        pk.append_at(kc, vc, kn, vn, tables, pos, slots)  # slot mapping + K/V append, one launch
         if ev is not None:
             ev[1].record()
         call.partitions()

@@ -107,6 +107,29 @@ PKV_API int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, con
                     void* stream);
 
 /*
+ * paged_kv_append_at — paged_kv_slot_mapping and paged_kv_append in one launch
+ * (the same two passages).  For every sequence s, with p = positions[s]: when
+ * 0 <= p < max_blocks_per_seq * block_size and the table entry
+ * T[s][p / block_size] lies in [0, num_blocks), copies k_new[s] and v_new[s]
+ * bit for bit to slot T[s][p / block_size] * block_size + p % block_size of
+ * k_cache and v_cache; otherwise writes nothing.  When slot_mapping is not
+ * NULL it receives that slot, or -1.
+ *
+ *   k_cache, v_cache [num_blocks, block_size, kv_heads, head_dim] dtype, in/out.
+ *   k_new, v_new     [num_seqs, kv_heads, head_dim] dtype, read.
+ *   block_tables     [num_seqs, max_blocks_per_seq] int32, read at column p / B only.
+ *   positions        [num_seqs] int32.
+ *   slot_mapping     [num_seqs] int32, written, or NULL.
+ * Requires num_blocks * block_size <= INT32_MAX and kv_heads * head_dim *
+ * element size a multiple of 16 bytes.  Errors: PKV_ERR_NULL, PKV_ERR_SHAPE,
+ * PKV_ERR_DTYPE; num_seqs == 0 enqueues nothing.
+ */
+PKV_API int paged_kv_append_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                               const int32_t* block_tables, const int32_t* positions, int32_t* slot_mapping,
+                               int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                               int32_t block_size, int32_t kv_heads, int32_t head_dim, int32_t dtype, void* stream);
+
+/*
  * paged_attn_decode — one decode step of paged attention, [B] section 2 with
  * the table walk of [A].  For every sequence s (L = context_lens[s]) and query
  * head h (kv head g = h / (q_heads / kv_heads)):

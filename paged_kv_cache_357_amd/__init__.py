@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     DecodeCall,
     PagedKVError,
     append,
+    append_at,
     decode,
     load_library,
     plan,

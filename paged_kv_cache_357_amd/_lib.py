@@ -28,6 +28,8 @@ _DECODE_ARGS = [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c
 SIGNATURES = {
     "paged_kv_slot_mapping": (_c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "paged_kv_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
+    "paged_kv_append_at": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                    _c_i32, _c_i32, _vp]),
     "paged_attn_decode": (_c_int, _DECODE_ARGS),
     "paged_attn_decode_partitions": (_c_int, _DECODE_ARGS),
     "paged_attn_decode_reduce": (_c_int, _DECODE_ARGS),
@@ -120,6 +122,29 @@ def append(k_cache, v_cache, k_new, v_new, slot_mapping_t) -> None:
     _check("paged_kv_append", lib.paged_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                                                   _ptr(slot_mapping_t), N, NB, B, Hkv, D, _DTYPES[k_cache.dtype],
                                                   _stream(dev)))
+
+
+def append_at(k_cache, v_cache, k_new, v_new, block_tables, positions, slot_mapping_out=None) -> None:
+    """Write k_new[s] / v_new[s] at position positions[s] of sequence s (slot
+    computed from the block table in the same launch); optionally record the
+    slots in slot_mapping_out."""
+    lib = load_library()
+    NB, B, Hkv, D = k_cache.shape
+    S, MB = block_tables.shape
+    _require(v_cache.shape == k_cache.shape, "k_cache and v_cache differ in shape")
+    _require(k_new.shape == (S, Hkv, D) and v_new.shape == (S, Hkv, D), "k_new/v_new must be [num_seqs, Hkv, D]")
+    _require(block_tables.dtype == torch.int32 and positions.dtype == torch.int32, "int32 tables and positions")
+    _require(positions.shape == (S,), "positions must be [num_seqs]")
+    _require(len({k_cache.dtype, v_cache.dtype, k_new.dtype, v_new.dtype}) == 1, "mixed dtypes")
+    _require(k_cache.dtype in _DTYPES, f"unsupported dtype {k_cache.dtype}")
+    tensors = [k_cache, v_cache, k_new, v_new, block_tables, positions]
+    if slot_mapping_out is not None:
+        _require(slot_mapping_out.dtype == torch.int32 and slot_mapping_out.shape == (S,), "slots must be int32 [S]")
+        tensors.append(slot_mapping_out)
+    dev = _dev(*tensors)
+    _check("paged_kv_append_at", lib.paged_kv_append_at(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                                        _ptr(block_tables), _ptr(positions), _ptr(slot_mapping_out),
+                                                        S, MB, NB, B, Hkv, D, _DTYPES[k_cache.dtype], _stream(dev)))
 
 
 def _decode_shapes(q, k_cache, v_cache, block_tables, context_lens):

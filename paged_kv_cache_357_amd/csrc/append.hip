@@ -50,7 +50,52 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ kc, char
   reinterpret_cast<uint4*>(vc + (size_t)slot * row)[c] = vv;
 }
 
+// Slot mapping and append in one pass: thread (t, c) computes the slot of
+// sequence t's position itself (every thread of the row gets the same value
+// from the same two loads), copies column c, and column 0 records the slot.
+// A position outside the table or a block id outside the pool gives slot -1
+// and no write.
+__global__ __launch_bounds__(256) void append_at_kernel(char* __restrict__ kc, char* __restrict__ vc,
+                                                        const char* __restrict__ kn, const char* __restrict__ vn,
+                                                        const int32_t* __restrict__ tables,
+                                                        const int32_t* __restrict__ positions,
+                                                        int32_t* __restrict__ slots, int N, int MB, int B, int NB,
+                                                        int cols16) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long t = gid / cols16;
+  const int c = (int)(gid - t * cols16);
+  if (t >= N) return;
+  const int p = positions[t];
+  int slot = -1;
+  if (p >= 0 && (long long)p < (long long)MB * B) {
+    const int b = p / B;
+    const int blk = tables[(size_t)t * MB + b];
+    if (blk >= 0 && blk < NB) slot = blk * B + (p - b * B);
+  }
+  if (slots != nullptr && c == 0) slots[t] = slot;
+  if (slot < 0) return;
+  const size_t row = (size_t)cols16 * 16;
+  const uint4 kv = reinterpret_cast<const uint4*>(kn + (size_t)t * row)[c];
+  const uint4 vv = reinterpret_cast<const uint4*>(vn + (size_t)t * row)[c];
+  reinterpret_cast<uint4*>(kc + (size_t)slot * row)[c] = kv;
+  reinterpret_cast<uint4*>(vc + (size_t)slot * row)[c] = vv;
+}
+
 }  // namespace
+
+hipError_t launch_append_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* tables, const int32_t* positions, int32_t* slots, int N, int MB, int B,
+                            int NB, int row_bytes, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int cols16 = row_bytes / 16;
+  const long long total = (long long)N * cols16;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(append_at_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, static_cast<char*>(k_cache),
+                     static_cast<char*>(v_cache), static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+                     tables, positions, slots, N, MB, B, NB, cols16);
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* tables, const int32_t* positions, int S, int MB,
                                int B, hipStream_t stream) {

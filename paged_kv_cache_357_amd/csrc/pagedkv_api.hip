@@ -184,6 +184,25 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void*
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_kv_append_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                       const int32_t* block_tables, const int32_t* positions, int32_t* slot_mapping,
+                       int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t block_size,
+                       int32_t kv_heads, int32_t head_dim, int32_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0 || kv_heads <= 0 ||
+      head_dim <= 0)
+    return PKV_ERR_SHAPE;
+  if ((long long)num_blocks * block_size > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  const long long row = (long long)kv_heads * head_dim * elt_bytes(dtype);
+  if (row % 16 || row > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !block_tables || !positions) return PKV_ERR_NULL;
+  const hipError_t e = pkv::launch_append_at(k_cache, v_cache, k_new, v_new, block_tables, positions, slot_mapping,
+                                             num_seqs, max_blocks_per_seq, block_size, num_blocks, (int)row,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t max_context_len, int32_t dtype, int32_t partition_size,
                            int32_t* resolved_partition_size, int32_t* num_partitions) {

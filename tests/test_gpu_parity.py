@@ -70,6 +70,44 @@ def test_small_slots_append_then_decode(pk, k):
     assert_parity(out, ref, w, what="decode(L+1) after append")
 
 
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_small_append_at_matches_oracle(pk, k):
+    """The one-launch slot mapping + append: slots and pools bit for bit
+    against the oracle, with positions outside the table, negative ones and a
+    table entry outside the pool turned into slot -1 and no write."""
+    w = make_small(k)
+    d = to_gpu(w)
+    B, MB = w.block_size, w.block_tables.shape[1]
+    pos = w.context_lens.astype(np.int64).copy()
+    tables = w.block_tables.copy()
+    bad = set()
+    if w.num_seqs >= 4:
+        pos[1] = -3
+        pos[2] = MB * B          # one past the table
+        tables[3, pos[3] // B] = w.num_blocks + 5
+        bad = {1, 2, 3}
+    d.tables = torch.from_numpy(np.ascontiguousarray(tables)).cuda()
+    pos_t = torch.from_numpy(pos.astype(np.int32)).cuda()
+    slots_t = torch.full((w.num_seqs,), 12345, dtype=torch.int32, device="cuda")
+    pk.append_at(d.k, d.v, d.kn, d.vn, d.tables, pos_t, slots_t)
+    torch.cuda.synchronize()
+    good = [s for s in range(w.num_seqs) if s not in bad]
+    want = np.full(w.num_seqs, -1, dtype=np.int64)
+    want[good] = pa.oracle_slot_mapping(w.block_tables[good], pos[good], B)
+    assert np.array_equal(slots_t.cpu().numpy().astype(np.int64), want)
+    keep = np.where(np.isin(np.arange(w.num_seqs), good), pos, -1)
+    k2, v2 = pa.oracle_append(raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables, keep,
+                              raw_numpy(w.k_new), raw_numpy(w.v_new), B)
+    assert np.array_equal(raw_numpy(d.k.cpu()).view(np.uint8), k2.view(np.uint8))
+    assert np.array_equal(raw_numpy(d.v.cpu()).view(np.uint8), v2.view(np.uint8))
+    # without the slot output, the same writes
+    d2 = to_gpu(w)
+    d2.tables = d.tables
+    pk.append_at(d2.k, d2.v, d2.kn, d2.vn, d2.tables, pos_t)
+    torch.cuda.synchronize()
+    assert torch.equal(d2.k, d.k) and torch.equal(d2.v, d.v)
+
+
 def test_stages_equal_whole_call(pk):
     w = make_small(5)
     d = to_gpu(w)
@@ -141,6 +179,35 @@ def test_full_config(pk, k):
     ref1 = oracle_out(w, lens=lens1, seqs=seqs1, k_cache=k2, v_cache=v2)
     assert_parity(out1, ref1, w, seqs=seqs1, what="decode(L+1) after append")
     _FULL.pop(k, None)  # the pools now differ from the generator's
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_full_append_at(pk, k):
+    """The one-launch slot write at full size: equal, bit for bit, to the
+    oracle's slots and to the rows each slot should hold; every other row,
+    and every shared prompt block, untouched."""
+    w, d = full(k)
+    B = w.block_size
+    slots_t = torch.empty(w.num_seqs, dtype=torch.int32, device="cuda")
+    before_k = d.k.clone()
+    pk.append_at(d.k, d.v, d.kn, d.vn, d.tables, d.lens, slots_t)
+    torch.cuda.synchronize()
+    slots = slots_t.cpu().numpy().astype(np.int64)
+    assert np.array_equal(slots, pa.oracle_slot_mapping(w.block_tables, w.context_lens, B))
+    ib = torch.int16 if w.dtype == "bf16" else torch.int32
+    idx = torch.from_numpy(slots).cuda()
+    mask = torch.ones(w.num_blocks * B, dtype=torch.bool, device="cuda")
+    mask[idx] = False
+    flat = d.k.view(w.num_blocks * B, -1).view(ib)
+    assert torch.equal(flat.index_select(0, idx), d.kn.reshape(len(slots), -1).view(ib))
+    assert torch.equal(flat[mask], before_k.view(w.num_blocks * B, -1).view(ib)[mask])
+    del before_k
+    flat_v = d.v.view(w.num_blocks * B, -1).view(ib)
+    assert torch.equal(flat_v.index_select(0, idx), d.vn.reshape(len(slots), -1).view(ib))
+    if k == 4:
+        shared = torch.from_numpy(np.unique(w.block_tables[:, :w.meta["prompt_blocks"]]).astype(np.int64))
+        assert torch.equal(d.v.index_select(0, shared.cuda()).cpu(), w.v_cache.index_select(0, shared))
+    _FULL.pop(k, None)
 
 
 def test_full_long_context_partition_sizes(pk):
