@@ -14,7 +14,8 @@ step appends the token at position L and attends over L + 1 tokens.
 prints one JSON line: KV GB/s of the whole step (logical K+V bytes read by
 the attention, sum(L+1) * 2 * kv_heads * head_dim * 2 B, per step time), the
 roofline of the dominant kernel (stage 1, its duration from HIP events
-recorded around it on the launch stream inside the timed region; its HBM
+recorded around it on the launch stream inside the timed region, created
+without the system-scope fence that default events add; its HBM
 traffic from the committed rocprofv3 counter summary when that was taken on
 the same kernel source), and the fp64 CPU oracle timed on the host's cores
 over the same workload.
@@ -62,6 +63,54 @@ def parse():
                          "workload's run with --copy-probe-mib into its traffic summary under profiles/")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the copy probe in those runs")
     return ap.parse_args()
+
+
+class HipEvents:
+    """Timing events of the HIP runtime already loaded in this process,
+    recorded on a given stream (the one the kernels are launched on).  They
+    are created with hipEventDisableSystemFence: recording one then costs no
+    system-scope cache writeback and invalidation, which with default events
+    adds several microseconds to every step and disturbs the work that
+    follows.  Used only for timing; the host synchronises with the device
+    before reading them."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n, stream_ptr):
+        import ctypes
+        path = "libamdhip64.so.7"
+        with open("/proc/self/maps") as f:  # the copy torch loaded
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.stream = ctypes.c_void_p(stream_ptr)
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+            self.ev.append(e)
+
+    def record(self, i):
+        rc = self.hip.hipEventRecord(self.ev[i], self.stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def ms(self, i, j):
+        t = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(t), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(t.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def kernel_sha() -> str:
@@ -250,34 +299,47 @@ def main():
     P, NP = call.plan
     balanced = P == 0  # balanced schedule: NP is the number of worker waves
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    stream_ptr = torch.cuda.current_stream(dev).cuda_stream  # the stream every entry point launches on
+
+    def step(ev=None, i=0):
         pk.append_at(kc, vc, kn, vn, tables, pos, slots)  # slot mapping + K/V append, one launch
         if ev is not None:
-            ev[1].record()
+            ev.record(2 * i)
         call.partitions()
         if ev is not None:
-            ev[2].record()
+            ev.record(2 * i + 1)
         call.reduce()
-        if ev is not None:
-            ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: K whole steps; two events per step bracket the stage-1 launch.
+    ev = HipEvents(2 * args.steps, stream_ptr)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(ev, i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    part_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    red_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-    app_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    part_ms = float(np.mean([ev.ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+    ev.close()
+
+    # After the timed region: the other two launches, each bracketed alone.
+    ev = HipEvents(4 * 10, stream_ptr)
+    for i in range(10):
+        ev.record(4 * i)
+        pk.append_at(kc, vc, kn, vn, tables, pos, slots)
+        ev.record(4 * i + 1)
+        call.partitions()
+        ev.record(4 * i + 2)
+        call.reduce()
+        ev.record(4 * i + 3)
+    torch.cuda.synchronize()
+    app_ms = float(np.mean([ev.ms(4 * i, 4 * i + 1) for i in range(10)]))
+    red_ms = float(np.mean([ev.ms(4 * i + 2, 4 * i + 3) for i in range(10)]))
+    ev.close()
 
     kv_bytes = w.kv_bytes(lens_step)
     tokens = int(lens_step.astype(np.int64).sum())
@@ -290,7 +352,8 @@ def main():
         "pct_of_hbm_peak_step": 100.0 * value / HBM_PEAK_GBS,
         "seq_tokens_per_s": tokens / (ms_step / 1e3),
         "decode_tokens_per_s": w.num_seqs / (ms_step / 1e3),
-        "partition_kernel_ms": part_ms, "reduce_kernel_ms": red_ms, "slot_map_append_ms": app_ms,
+        "partition_kernel_ms": part_ms, "reduce_kernel_ms_untimed": red_ms,
+        "append_at_kernel_ms_untimed": app_ms,
         "schedule": "balanced" if balanced else "partitioned",
         "partition_size": P, "num_partitions": NP,
         "kernel_sha": kernel_sha(),
@@ -298,16 +361,15 @@ def main():
 
     if args.flush_reps > 0:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        times = []
-        for _ in range(args.flush_reps):
+        fev = HipEvents(2 * args.flush_reps, stream_ptr)
+        for i in range(args.flush_reps):
             flush.fill_(1)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
+            fev.record(2 * i)
             call.run()
-            b.record()
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        med = float(np.median(times))
+            fev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        med = float(np.median([fev.ms(2 * i, 2 * i + 1) for i in range(args.flush_reps)]))
+        fev.close()
         extra["flushed_decode_ms_median"] = med
         extra["flushed_decode_GBps"] = kv_bytes / (med / 1e3) / 1e9
         del flush
@@ -343,15 +405,14 @@ def main():
                              ("copy", lambda: plib.pkv_probe_copy(ctypes.c_void_p(dst.data_ptr()),
                                                                  ctypes.c_void_p(buf.data_ptr()),
                                                                  ctypes.c_size_t(nb // 2), stream))):
-                ts = []
-                for _ in range(6):
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record()
+                pev = HipEvents(12, stream_ptr)
+                for i in range(6):
+                    pev.record(2 * i)
                     assert fn() == 0
-                    b.record()
-                    torch.cuda.synchronize()
-                    ts.append(a.elapsed_time(b))
-                t = float(np.median(ts[1:]))
+                    pev.record(2 * i + 1)
+                torch.cuda.synchronize()
+                t = float(np.median([pev.ms(2 * i, 2 * i + 1) for i in range(1, 6)]))
+                pev.close()
                 moved = nb if name == "read" else nb  # copy: nb/2 read + nb/2 written
                 res[name + "_GBps"] = moved / (t / 1e3) / 1e9
             extra["probe"] = res

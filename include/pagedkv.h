@@ -139,12 +139,18 @@ PKV_API int paged_kv_append_at(void* k_cache, void* v_cache, const void* k_new, 
  *
  * where K_i / V_i are read from slot T[s][i / B] * B + i % B.  Scores, the
  * online softmax and the V accumulation are fused in one pass over each
- * sequence's physical blocks, all in fp32; long contexts are split into
- * partitions of `partition_size` tokens whose partial results are merged by a
- * second kernel (log-sum-exp rescaling).  The result does not depend on which
- * physical blocks hold the tokens: reductions follow logical positions only,
- * so permuting the pool, or sharing blocks between sequences, gives bitwise
- * identical outputs, and repeated calls are bitwise deterministic.
+ * sequence's physical blocks, all in fp32.  Two schedules split the work:
+ *   - balanced (partition_size 0, some L above 512 tokens, num_seqs <= 2048):
+ *     the 16-token chunks of all (sequence, kv head) pairs, laid end to end,
+ *     are cut into one equal share per resident worker;
+ *   - partitioned (otherwise): partitions of `partition_size` tokens, one
+ *     wave each.
+ * Pieces of a (sequence, kv head) pair computed apart are merged by a second
+ * kernel (log-sum-exp rescaling).  Which tokens each piece holds depends on
+ * the lengths and the plan only, so repeated calls are bitwise deterministic;
+ * the result does not depend on which physical blocks hold the tokens
+ * (reductions follow logical positions only), so permuting the pool, or
+ * sharing blocks between sequences, gives bitwise identical outputs.
  *
  *   out          [num_seqs, q_heads, head_dim] fp32, written (every element).
  *   q            [num_seqs, q_heads, head_dim] dtype.
@@ -179,11 +185,13 @@ PKV_API int paged_attn_decode(float* out, const void* q, const void* k_cache, co
 /*
  * The two stages of paged_attn_decode, for callers that time or schedule them
  * apart.  Same arguments and checks.  Stage 1 runs the fused score / online
- * softmax / V pass per (sequence, kv head, partition); when the resolved plan
- * has a single partition it writes `out` directly and stage 2 enqueues
- * nothing.  Otherwise stage 1 writes per-partition (max, sum, accumulator)
- * triples to the workspace and stage 2 merges them into `out`.  Stage 2 must
- * follow stage 1 on the same stream with the same arguments.
+ * softmax / V pass; when the resolved plan is partitioned with a single
+ * partition it writes `out` directly and stage 2 enqueues nothing.
+ * Otherwise stage 1 writes the rows it finishes alone to `out` and partial
+ * (max, sum, accumulator) records of split pairs to the workspace, and
+ * stage 2 merges those into `out` (and writes the rows of invalid and empty
+ * sequences).  Stage 2 must follow stage 1 on the same stream with the same
+ * arguments and lengths.
  */
 PKV_API int paged_attn_decode_partitions(float* out, const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_tables, const int32_t* context_lens,
@@ -200,10 +208,12 @@ PKV_API int paged_attn_decode_reduce(float* out, const void* q, const void* k_ca
                              size_t workspace_bytes, void* stream);
 
 /*
- * paged_attn_decode_plan — the partition size and partition count a call with
- * these arguments uses (partition_size 0 = the automatic choice).  Host only;
- * writes *resolved_partition_size and *num_partitions (either may be NULL).
- * Returns PKV_OK or the error the decode call would return for these sizes.
+ * paged_attn_decode_plan — the schedule a call with these arguments uses
+ * (partition_size 0 = the automatic choice).  Host only; writes
+ * *resolved_partition_size and *num_partitions (either may be NULL):
+ * (P, partitions per sequence) for the partitioned schedule, (0, worker
+ * waves) for the balanced one.  Returns PKV_OK or the error the decode call
+ * would return for these sizes.
  */
 PKV_API int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t max_context_len, int32_t dtype,
@@ -212,9 +222,12 @@ PKV_API int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv
 
 /*
  * paged_attn_decode_workspace_size — bytes of workspace paged_attn_decode needs
- * for these arguments: 0 when the plan has a single partition, else
- * num_seqs * q_heads * num_partitions * (head_dim + 2) * 4 bytes (rounded up
- * to 256).  Host only.  Returns 0 for arguments the decode call would reject.
+ * for these arguments.  Partitioned: 0 for a single partition, else
+ * num_seqs * q_heads * num_partitions * (head_dim + 2) * 4 bytes (each part
+ * rounded up to 256).  Balanced: partial records for W worker waves (two
+ * records of group-size rows each, head_dim + 2 floats per row) and
+ * (num_seqs + 1) * 4 bytes of chunk prefix sums.  Host only.  Returns 0 for
+ * arguments the decode call would reject.
  */
 PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
                                         int32_t head_dim, int32_t block_size, int32_t max_context_len,
