@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--probes", action="store_true", help="also time plain HBM read / copy probes")
     ap.add_argument("--flush-reps", type=int, default=0,
                     help="also time this many single decode launches after a 1 GiB cache flush each")
+    ap.add_argument("--cow-pairs", type=int, default=2048,
+                    help="block pairs in the copy-on-write block copy timed after the step (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain copy of this size (reference kernel for byte counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -358,6 +360,34 @@ def main():
         "partition_size": P, "num_partitions": NP,
         "kernel_sha": kernel_sha(),
     }
+
+    if args.cow_pairs > 0:
+        # Copy-on-write block copy at this workload's block shape, on buffers
+        # of its own: pair i copies block i to block n + i of both caches.
+        n = args.cow_pairs
+        shape = (2 * n, w.block_size, w.kv_heads, w.head_dim)
+        ck = torch.empty(shape, dtype=kc.dtype, device=dev)
+        cv = torch.empty(shape, dtype=kc.dtype, device=dev)
+        ck.fill_(1)
+        cv.fill_(2)
+        src = torch.arange(n, dtype=torch.int32, device=dev)
+        dst = src + n
+        for _ in range(2):
+            pk.copy_blocks(ck, cv, src, dst)
+        cev = HipEvents(2 * 10, stream_ptr)
+        for i in range(10):
+            cev.record(2 * i)
+            pk.copy_blocks(ck, cv, src, dst)
+            cev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        cms = float(np.mean([cev.ms(2 * i, 2 * i + 1) for i in range(10)]))
+        cev.close()
+        block_bytes = w.block_size * w.kv_heads * w.head_dim * kc.element_size()
+        moved = 2 * n * 2 * block_bytes  # K and V blocks, each read once and written once
+        extra["copy_blocks"] = {"kernel": "copy_blocks_kernel", "pairs": n, "block_bytes": block_bytes,
+                                "bytes_moved": moved, "ms": cms, "GBps": moved / (cms / 1e3) / 1e9,
+                                "frac_of_hbm_peak": moved / (cms / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del ck, cv
 
     if args.flush_reps > 0:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

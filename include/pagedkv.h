@@ -60,7 +60,10 @@ enum pkv_status {
   PKV_ERR_UNSUPPORTED = -4, /* valid but outside the compiled set (head_dim,
                                block size, group size, partition size)            */
   PKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
-  PKV_ERR_HIP = -6          /* a kernel launch failed                             */
+  PKV_ERR_HIP = -6,         /* a kernel launch failed                             */
+  PKV_ERR_OUT_OF_BLOCKS = -7, /* block manager: the free pool (or a table's
+                               max_blocks_per_seq) cannot hold the request      */
+  PKV_ERR_BAD_SEQUENCE = -8 /* block manager: not a live sequence id              */
 };
 
 enum pkv_dtype {
@@ -232,6 +235,86 @@ PKV_API int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv
 PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
                                         int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                         int32_t dtype, int32_t partition_size);
+
+/*
+ * paged_kv_copy_blocks — the block copy of copy-on-write ("PagedAttention and
+ * vLLM Architecture: Virtual Memory for LLM Serving", section 3: a stream that
+ * must write into a shared block first gets a fresh block holding a copy of
+ * it).  For every pair i with both ids in [0, num_blocks), copies block
+ * src[i] of k_cache to block dst[i] of k_cache, and the same in v_cache, bit
+ * for bit (all block_size token rows); pairs with an id outside the pool are
+ * skipped.
+ *
+ *   k_cache, v_cache [num_blocks, block_size, kv_heads, head_dim] dtype, in/out.
+ *   src, dst         [n_pairs] int32, device.  The dst blocks must be distinct
+ *                    and none may be a src of the same call (the pairs run in
+ *                    parallel); the block manager's copies always satisfy this.
+ * kv_heads * head_dim * element size must be a multiple of 16 bytes.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE; n_pairs == 0 enqueues
+ * nothing.
+ */
+PKV_API int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                                 int32_t n_pairs, int32_t num_blocks, int32_t block_size, int32_t kv_heads,
+                                 int32_t head_dim, int32_t dtype, void* stream);
+
+/*
+ * Block manager — host-side bookkeeping of the physical block pool
+ * ("PagedAttention and vLLM Architecture: Virtual Memory for LLM Serving",
+ * section 1: a pool of fixed-size blocks set up at start and a per-request
+ * block table kept by the engine; "Why Internal Fragmentation is Bounded": a
+ * block is added only when a token overflows the last one; section 3: forked
+ * streams share blocks under a reference count, and a write into a shared
+ * block first moves the writer to a private copy and lowers the count).
+ *
+ * All pointers here are HOST pointers; nothing touches the device.  The free
+ * pool hands out the lowest-numbered free block first.  A fork makes one
+ * child that shares every block of its parent.  Sequence ids count up from 0
+ * and are never reused.  A call that fails returns a negative status and
+ * changes nothing (pkv_bm_append_batch: nothing beyond the first *n_done
+ * sequences).  One manager must not be used from two threads at once.
+ *
+ * pkv_bm_create         a pool of num_blocks blocks of block_size tokens, tables of
+ *                       at most max_blocks_per_seq blocks; NULL on bad sizes
+ *                       (num_blocks * block_size must fit int32) or no memory.
+ * pkv_bm_add_sequence   a new empty sequence; its id in *seq.
+ * pkv_bm_fork           a new sequence sharing all blocks (and the length) of parent.
+ * pkv_bm_free           drops a sequence; blocks no sequence holds return to the pool.
+ * pkv_bm_append         reserves the slots of n_tokens new tokens of seq (positions
+ *                       L .. L+n_tokens-1) in slots[n_tokens].  When the first of
+ *                       them falls into a block shared with another sequence, a
+ *                       fresh block replaces it in seq's table and the copy
+ *                       (copy_src[0] -> copy_dst[0]) is reported in *n_copies (0 or
+ *                       1); run it with paged_kv_copy_blocks before writing the
+ *                       tokens.  PKV_ERR_OUT_OF_BLOCKS when the pool or the table
+ *                       limit cannot hold them.
+ * pkv_bm_append_batch   one new token for each of seqs[0..n_seqs-1], in order
+ *                       (the decode step): slots[n_seqs]; copies (at most one per
+ *                       sequence) in copy_src/copy_dst[*n_copies]; *n_done sequences
+ *                       were served before any failure.
+ * pkv_bm_table          seq's block ids into blocks[capacity] (*n_blocks of them) and
+ *                       its length into *length (may be NULL).
+ * pkv_bm_tables         the rows of seqs as an [n_seqs, max_blocks_per_seq] int32
+ *                       table padded with `fill`, and their lengths in lens[n_seqs],
+ *                       ready to upload for paged_attn_decode.
+ * pkv_bm_ref_count      sequences holding a block.
+ * pkv_bm_free_blocks    blocks in the free pool (-1 for a NULL manager).
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+PKV_API pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq);
+PKV_API void pkv_bm_destroy(pkv_block_manager* m);
+PKV_API int pkv_bm_add_sequence(pkv_block_manager* m, int32_t* seq);
+PKV_API int pkv_bm_fork(pkv_block_manager* m, int32_t parent, int32_t* child);
+PKV_API int pkv_bm_free(pkv_block_manager* m, int32_t seq);
+PKV_API int pkv_bm_append(pkv_block_manager* m, int32_t seq, int32_t n_tokens, int32_t* slots, int32_t* copy_src,
+                          int32_t* copy_dst, int32_t* n_copies);
+PKV_API int pkv_bm_append_batch(pkv_block_manager* m, const int32_t* seqs, int32_t n_seqs, int32_t* slots,
+                                int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies, int32_t* n_done);
+PKV_API int pkv_bm_table(const pkv_block_manager* m, int32_t seq, int32_t* blocks, int32_t capacity,
+                         int32_t* n_blocks, int64_t* length);
+PKV_API int pkv_bm_tables(const pkv_block_manager* m, const int32_t* seqs, int32_t n_seqs, int32_t* tables,
+                          int32_t max_blocks_per_seq, int32_t fill, int32_t* lens);
+PKV_API int pkv_bm_ref_count(const pkv_block_manager* m, int32_t block, int32_t* ref);
+PKV_API int32_t pkv_bm_free_blocks(const pkv_block_manager* m);
 
 /* paged_status_str — a static, human-readable name for a status code. */
 PKV_API const char* paged_status_str(int status);

@@ -19,3 +19,4 @@ from .paged_attention import (  # noqa: F401
     oracle_decode,
     oracle_decode_sampled,
 )
+from .block_manager import OutOfBlocks, RefBlockManager, copy_blocks  # noqa: F401,E402

@@ -1,10 +1,14 @@
-"""Paged KV-cache decode attention and KV append for MI355X (gfx950).
+"""Paged KV-cache decode attention, KV append and block management for MI355X
+(gfx950).
 
 The computation lives in hand-written HIP kernels behind the C ABI of
 libpagedkv.so (include/pagedkv.h); this package is its Python binding.
 """
 from ._lib import (  # noqa: F401
     DTYPE_BF16,
+    BlockManager,
+    OutOfBlocksError,
+    copy_blocks,
     DTYPE_F32,
     LIB_PATH,
     SIGNATURES,

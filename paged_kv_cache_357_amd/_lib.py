@@ -36,7 +36,21 @@ SIGNATURES = {
     "paged_attn_decode_plan": (_c_int, [_c_i32] * 8 + [_i32p, _i32p]),
     "paged_attn_decode_workspace_size": (_c_sz, [_c_i32] * 8),
     "paged_status_str": (ctypes.c_char_p, [_c_int]),
+    "paged_kv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp] + [_c_i32] * 6 + [_vp]),
+    "pkv_bm_create": (_vp, [_c_i32] * 3),
+    "pkv_bm_destroy": (None, [_vp]),
+    "pkv_bm_add_sequence": (_c_int, [_vp, _i32p]),
+    "pkv_bm_fork": (_c_int, [_vp, _c_i32, _i32p]),
+    "pkv_bm_free": (_c_int, [_vp, _c_i32]),
+    "pkv_bm_append": (_c_int, [_vp, _c_i32, _c_i32, _i32p, _i32p, _i32p, _i32p]),
+    "pkv_bm_append_batch": (_c_int, [_vp, _i32p, _c_i32, _i32p, _i32p, _i32p, _i32p, _i32p]),
+    "pkv_bm_table": (_c_int, [_vp, _c_i32, _i32p, _c_i32, _i32p, ctypes.POINTER(ctypes.c_int64)]),
+    "pkv_bm_tables": (_c_int, [_vp, _i32p, _c_i32, _i32p, _c_i32, _c_i32, _i32p]),
+    "pkv_bm_ref_count": (_c_int, [_vp, _c_i32, _i32p]),
+    "pkv_bm_free_blocks": (ctypes.c_int32, [_vp]),
 }
+
+PKV_ERR_OUT_OF_BLOCKS = -7
 
 _lib = None
 
@@ -145,6 +159,128 @@ def append_at(k_cache, v_cache, k_new, v_new, block_tables, positions, slot_mapp
     _check("paged_kv_append_at", lib.paged_kv_append_at(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                                                         _ptr(block_tables), _ptr(positions), _ptr(slot_mapping_out),
                                                         S, MB, NB, B, Hkv, D, _DTYPES[k_cache.dtype], _stream(dev)))
+
+
+def copy_blocks(k_cache, v_cache, src, dst) -> None:
+    """Copy block src[i] -> dst[i] of both caches (copy-on-write copies)."""
+    lib = load_library()
+    NB, B, Hkv, D = k_cache.shape
+    _require(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache and v_cache differ")
+    _require(k_cache.dtype in _DTYPES, f"unsupported dtype {k_cache.dtype}")
+    _require(src.dtype == torch.int32 and dst.dtype == torch.int32 and src.shape == dst.shape and src.dim() == 1,
+             "src and dst must be int32 vectors of one length")
+    dev = _dev(k_cache, v_cache, src, dst)
+    _check("paged_kv_copy_blocks", lib.paged_kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src), _ptr(dst),
+                                                            src.numel(), NB, B, Hkv, D, _DTYPES[k_cache.dtype],
+                                                            _stream(dev)))
+
+
+class OutOfBlocksError(PagedKVError):
+    pass
+
+
+def _i32buf(n):
+    import numpy as np
+    return np.zeros(max(1, n), dtype=np.int32)
+
+
+def _p(a):
+    return a.ctypes.data_as(_i32p)
+
+
+class BlockManager:
+    """Host-side block manager of the library (pool, tables, reference counts,
+    copy-on-write decisions).  ``append`` returns the slots of the new tokens
+    and the (src, dst) block copies to run with :func:`copy_blocks` first."""
+
+    def __init__(self, num_blocks, block_size, max_blocks_per_seq):
+        self.lib = load_library()
+        self.num_blocks, self.B, self.max_blocks = int(num_blocks), int(block_size), int(max_blocks_per_seq)
+        self.h = self.lib.pkv_bm_create(self.num_blocks, self.B, self.max_blocks)
+        if not self.h:
+            raise ValueError("pkv_bm_create rejected the sizes")
+        self._live = set()
+
+    def __del__(self):
+        h, self.h = getattr(self, "h", None), None
+        if h:
+            self.lib.pkv_bm_destroy(h)
+
+    def _st(self, fn, st):
+        if st == PKV_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocksError(fn, st)
+        _check(fn, st)
+
+    def add_sequence(self):
+        out = ctypes.c_int32()
+        self._st("pkv_bm_add_sequence", self.lib.pkv_bm_add_sequence(self.h, ctypes.byref(out)))
+        self._live.add(out.value)
+        return out.value
+
+    def fork(self, parent):
+        out = ctypes.c_int32()
+        self._st("pkv_bm_fork", self.lib.pkv_bm_fork(self.h, int(parent), ctypes.byref(out)))
+        self._live.add(out.value)
+        return out.value
+
+    def free(self, s):
+        self._st("pkv_bm_free", self.lib.pkv_bm_free(self.h, int(s)))
+        self._live.discard(int(s))
+
+    def append(self, s, n):
+        slots, src, dst, nc = _i32buf(n), _i32buf(1), _i32buf(1), ctypes.c_int32()
+        self._st("pkv_bm_append", self.lib.pkv_bm_append(self.h, int(s), int(n), _p(slots), _p(src), _p(dst),
+                                                         ctypes.byref(nc)))
+        return [int(x) for x in slots[:n]], [(int(src[i]), int(dst[i])) for i in range(nc.value)]
+
+    def append_batch(self, seqs):
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = len(seqs)
+        slots, src, dst = _i32buf(n), _i32buf(n), _i32buf(n)
+        nc, nd = ctypes.c_int32(), ctypes.c_int32()
+        st = self.lib.pkv_bm_append_batch(self.h, _p(seqs), n, _p(slots), _p(src), _p(dst), ctypes.byref(nc),
+                                          ctypes.byref(nd))
+        self._st("pkv_bm_append_batch", st)
+        return slots[:n].copy(), src[:nc.value].copy(), dst[:nc.value].copy()
+
+    def table(self, s):
+        buf, nb, ln = _i32buf(self.max_blocks), ctypes.c_int32(), ctypes.c_int64()
+        self._st("pkv_bm_table", self.lib.pkv_bm_table(self.h, int(s), _p(buf), self.max_blocks, ctypes.byref(nb),
+                                                       ctypes.byref(ln)))
+        return [int(x) for x in buf[:nb.value]]
+
+    def length(self, s):
+        buf, nb, ln = _i32buf(self.max_blocks), ctypes.c_int32(), ctypes.c_int64()
+        self._st("pkv_bm_table", self.lib.pkv_bm_table(self.h, int(s), _p(buf), self.max_blocks, ctypes.byref(nb),
+                                                       ctypes.byref(ln)))
+        return int(ln.value)
+
+    def tables(self, seqs, max_blocks_per_seq=None, fill=0):
+        """[len(seqs), max_blocks_per_seq] int32 table and int32 lengths (host numpy)."""
+        import numpy as np
+        mb = self.max_blocks if max_blocks_per_seq is None else int(max_blocks_per_seq)
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        t = np.zeros((max(1, len(seqs)), mb), dtype=np.int32)
+        lens = _i32buf(len(seqs))
+        self._st("pkv_bm_tables", self.lib.pkv_bm_tables(self.h, _p(seqs), len(seqs), _p(t), mb, int(fill),
+                                                         _p(lens)))
+        return t[:len(seqs)], lens[:len(seqs)].copy()
+
+    def ref_count(self, block):
+        out = ctypes.c_int32()
+        self._st("pkv_bm_ref_count", self.lib.pkv_bm_ref_count(self.h, int(block), ctypes.byref(out)))
+        return out.value
+
+    @property
+    def ref(self):
+        return [self.ref_count(b) for b in range(self.num_blocks)]
+
+    def free_blocks(self):
+        return int(self.lib.pkv_bm_free_blocks(self.h))
+
+    def live(self):
+        return sorted(self._live)
 
 
 def _decode_shapes(q, k_cache, v_cache, block_tables, context_lens):

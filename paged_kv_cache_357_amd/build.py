@@ -23,22 +23,29 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", 
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
+# Host-only C++ (the block manager) is built with the host compiler.
+HOST_CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden", "-I", os.path.join(ROOT, "include")]
+
 LIBS = {
-    "libpagedkv.so": ["pagedkv_api.hip", "decode.hip", "append.hip"],
+    "libpagedkv.so": ["pagedkv_api.hip", "decode.hip", "append.hip", "block_manager.cpp"],
     "libpkv_probes.so": ["bench_probes.hip"],
 }
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [HOST_CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in (r.stderr or "").splitlines() if noise not in ln)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+        raise RuntimeError(f"{cmd[0]} failed on {src}:\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
     return obj

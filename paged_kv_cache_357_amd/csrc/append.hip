@@ -1,4 +1,4 @@
-// Slot mapping and KV append for gfx950.
+// Slot mapping, KV append and the copy-on-write block copy for gfx950.
 //
 // Slot of logical position p: T[p / B] * B + p % B ("PagedAttention Paper
 // Breakdown", section 2, Address Translation Formula).  A sequence holding L
@@ -81,7 +81,63 @@ __global__ __launch_bounds__(256) void append_at_kernel(char* __restrict__ kc, c
   reinterpret_cast<uint4*>(vc + (size_t)slot * row)[c] = vv;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Copy-on-write block copy ("PagedAttention and vLLM Architecture", section
+// 3): block src[pair] -> block dst[pair] of both caches.  blockIdx.y picks the
+// pair, blockIdx.x a 16 KiB slice of the block; each thread moves four
+// 16-byte vectors of K and four of V with all eight loads in flight.  The data
+// is touched once, so loads and stores are nontemporal.
+constexpr int kCopyPerThread = 4;
+constexpr int kCopyVecPerWG = 256 * kCopyPerThread;
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,
+                                                          const int32_t* __restrict__ src,
+                                                          const int32_t* __restrict__ dst, int NB, int vpb,
+                                                          long long block_bytes, int pair0) {
+  const int pair = pair0 + (int)blockIdx.y;
+  const int s = src[pair];
+  const int d = dst[pair];
+  if (s < 0 || s >= NB || d < 0 || d >= NB) return;
+  const u32x4* ks = reinterpret_cast<const u32x4*>(kc + (size_t)s * (size_t)block_bytes);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(vc + (size_t)s * (size_t)block_bytes);
+  u32x4* kd = reinterpret_cast<u32x4*>(kc + (size_t)d * (size_t)block_bytes);
+  u32x4* vd = reinterpret_cast<u32x4*>(vc + (size_t)d * (size_t)block_bytes);
+  const int base = (int)blockIdx.x * kCopyVecPerWG + (int)threadIdx.x;
+  u32x4 a[kCopyPerThread], b[kCopyPerThread];
+#pragma unroll
+  for (int i = 0; i < kCopyPerThread; ++i) {
+    const int j = base + i * 256;
+    if (j < vpb) {
+      a[i] = __builtin_nontemporal_load(ks + j);
+      b[i] = __builtin_nontemporal_load(vs + j);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyPerThread; ++i) {
+    const int j = base + i * 256;
+    if (j < vpb) {
+      __builtin_nontemporal_store(a[i], kd + j);
+      __builtin_nontemporal_store(b[i], vd + j);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int n_pairs,
+                              int num_blocks, long long block_bytes, hipStream_t stream) {
+  const int vpb = (int)(block_bytes / 16);
+  const unsigned gx = (unsigned)((vpb + kCopyVecPerWG - 1) / kCopyVecPerWG);
+  for (int p0 = 0; p0 < n_pairs; p0 += 65535) {  // grid y is at most 65535
+    const unsigned gy = (unsigned)((n_pairs - p0) < 65535 ? (n_pairs - p0) : 65535);
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, gy), dim3(256), 0, stream, static_cast<char*>(k_cache),
+                       static_cast<char*>(v_cache), src, dst, num_blocks, vpb, block_bytes, p0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_append_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* tables, const int32_t* positions, int32_t* slots, int N, int MB, int B,

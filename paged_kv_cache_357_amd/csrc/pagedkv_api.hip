@@ -203,6 +203,22 @@ int paged_kv_append_at(void* k_cache, void* v_cache, const void* k_new, const vo
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int32_t n_pairs,
+                         int32_t num_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                         void* stream) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (n_pairs < 0 || num_blocks <= 0 || block_size <= 0 || kv_heads <= 0 || head_dim <= 0) return PKV_ERR_SHAPE;
+  const long long row = (long long)kv_heads * head_dim * elt_bytes(dtype);
+  if (row % 16) return PKV_ERR_SHAPE;
+  const long long block_bytes = row * block_size;
+  if (block_bytes > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src || !dst) return PKV_ERR_NULL;
+  const hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, src, dst, n_pairs, num_blocks, block_bytes,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t max_context_len, int32_t dtype, int32_t partition_size,
                            int32_t* resolved_partition_size, int32_t* num_partitions) {
@@ -281,6 +297,8 @@ const char* paged_status_str(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch error";
+    case PKV_ERR_OUT_OF_BLOCKS: return "out of blocks";
+    case PKV_ERR_BAD_SEQUENCE: return "not a live sequence";
     default: return "unknown status";
   }
 }

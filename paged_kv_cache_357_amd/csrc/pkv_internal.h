@@ -90,6 +90,8 @@ hipError_t launch_slot_mapping(int32_t* slots, const int32_t* tables, const int3
                                int B, hipStream_t stream);
 hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                          const int32_t* slots, int N, long long num_slots, int row_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int n_pairs,
+                              int num_blocks, long long block_bytes, hipStream_t stream);
 hipError_t launch_append_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* tables, const int32_t* positions, int32_t* slots, int N, int MB, int B,
                             int NB, int row_bytes, hipStream_t stream);

@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -117,6 +117,13 @@ def test_append_and_slot_mapping_reject(lib):
     assert lib.paged_kv_slot_mapping(None, None, None, 4, 3, 16, 32, None) == -1
     assert lib.paged_kv_slot_mapping(fake, fake, fake, 4, 3, 16, 0x7fffffff, None) == -2
     assert lib.paged_kv_slot_mapping(None, None, None, 0, 3, 16, 32, None) == 0
+    f = lib.paged_kv_copy_blocks
+    assert f(None, None, None, None, 3, 32, 16, 4, 64, 0, None) == -1
+    assert f(fake, fake, fake, fake, 3, 32, 16, 4, 64, 5, None) == -3
+    assert f(fake, fake, fake, fake, 3, 32, 16, 1, 2, 1, None) == -2      # 4-byte rows
+    assert f(fake, fake, fake, fake, -1, 32, 16, 4, 64, 0, None) == -2
+    assert f(fake, fake, fake, fake, 3, 32, 1 << 20, 64, 128, 0, None) == -2  # a block over 2 GiB
+    assert f(None, None, None, None, 0, 32, 16, 4, 64, 0, None) == 0      # nothing to do
     f = lib.paged_kv_append_at
     assert f(None, None, None, None, None, None, None, 4, 3, 32, 16, 4, 64, 0, None) == -1
     assert f(fake, fake, fake, fake, fake, fake, None, 4, 3, 32, 16, 4, 64, 7, None) == -3

@@ -12,6 +12,7 @@ from .synth import (  # noqa: F401
     make_small,
     make_workload,
     raw_numpy,
+    normal_storage,
     identity_tables,
     permute_pool,
     poison_unused,

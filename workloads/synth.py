@@ -99,6 +99,12 @@ def _normal(rng, shape, dtype):
     return _to_storage(rng.standard_normal(shape, dtype=np.float32), dtype)
 
 
+def normal_storage(rng, shape, dtype: str) -> torch.Tensor:
+    """N(0,1) draws from rng stored in the cache dtype ("bf16" rounds to
+    nearest even), as a CPU tensor."""
+    return _normal(rng, shape, dtype)
+
+
 def make_workload(name, lens, q_heads, kv_heads, head_dim, block_size, dtype, seed, *,
                   rng=None, num_blocks=None, pool_factor=1.25, deal="shuffled",
                   prompts=None, tails=None, shared_q=False, pad_cols=0, values=True):
