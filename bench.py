@@ -35,6 +35,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, vendor figure
+
+# Prompt pass measured after the step: sequences, new tokens per sequence and
+# tokens held (the chunk continues an earlier context), Llama-7B heads.
+PREFILL_SHAPE = {"seqs": 4, "chunk": 1024, "context": 2048, "q_heads": 32, "kv_heads": 32, "head_dim": 128,
+                 "block_size": 16}
+
+
+def prefill_flops(seqs: int, chunk: int, context: int, q_heads: int, head_dim: int) -> int:
+    """4 D flops per (query row, head, visible key): 2 D for the score and 2 D
+    for the weighted V sum; the row at position p sees p + 1 keys."""
+    first = context - chunk
+    keys = chunk * (first + 1) + chunk * (chunk - 1) // 2  # sum of p + 1 over the chunk's positions
+    return 4 * head_dim * q_heads * keys * seqs
 METRIC = "paged decode attention: KV GB/s and % of MI355X HBM peak; seq-tokens/s"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_357_amd", "csrc", f) for f in ("decode.hip", "pkv_internal.h")]
@@ -58,6 +72,8 @@ def parse():
                     help="also time this many single decode launches after a 1 GiB cache flush each")
     ap.add_argument("--cow-pairs", type=int, default=2048,
                     help="block pairs in the copy-on-write block copy timed after the step (0 = skip)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prompt-pass (prefill) attention timed after the step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain copy of this size (reference kernel for byte counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -388,6 +404,37 @@ def main():
                                 "bytes_moved": moved, "ms": cms, "GBps": moved / (cms / 1e3) / 1e9,
                                 "frac_of_hbm_peak": moved / (cms / 1e3) / 1e9 / HBM_PEAK_GBS}
         del ck, cv
+
+    if not args.no_prefill:
+        from workloads import make_workload, normal_storage
+        ps = PREFILL_SHAPE
+        pw = make_workload("prefill-llama7b", [ps["context"]] * ps["seqs"], ps["q_heads"], ps["kv_heads"],
+                           ps["head_dim"], ps["block_size"], "bf16", 357100)
+        prng = np.random.default_rng(357101)
+        pq = normal_storage(prng, (ps["seqs"] * ps["chunk"], ps["q_heads"], ps["head_dim"]), "bf16").to(dev)
+        pk_, pv_ = pw.k_cache.to(dev), pw.v_cache.to(dev)
+        ptab = torch.from_numpy(pw.block_tables).to(dev)
+        plen = torch.from_numpy(pw.context_lens).to(dev)
+        pstart = torch.arange(0, ps["seqs"] + 1, dtype=torch.int32, device=dev) * ps["chunk"]
+        pout = torch.empty((ps["seqs"] * ps["chunk"], ps["q_heads"], ps["head_dim"]), dtype=torch.float32,
+                           device=dev)
+        for _ in range(2):
+            pk.prefill(pq, pk_, pv_, ptab, plen, pstart, pw.scale, ps["chunk"], ps["context"], out=pout)
+        pev = HipEvents(2 * 10, stream_ptr)
+        for i in range(10):
+            pev.record(2 * i)
+            pk.prefill(pq, pk_, pv_, ptab, plen, pstart, pw.scale, ps["chunk"], ps["context"], out=pout)
+            pev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        pms = float(np.mean([pev.ms(2 * i, 2 * i + 1) for i in range(10)]))
+        pev.close()
+        flops = prefill_flops(ps["seqs"], ps["chunk"], ps["context"], ps["q_heads"], ps["head_dim"])
+        tf = flops / (pms / 1e3) / 1e12
+        extra["prefill"] = {"kernel": "prefill_kernel", "shape": ps, "flops": flops, "ms": pms, "TFLOPs": tf,
+                            "bound": "mfma", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                            "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                            "tokens_per_s": ps["seqs"] * ps["chunk"] / (pms / 1e3)}
+        del pq, pk_, pv_, pout, pw
 
     if args.flush_reps > 0:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

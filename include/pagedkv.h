@@ -237,6 +237,43 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t q_head
                                         int32_t dtype, int32_t partition_size);
 
 /*
+ * paged_attn_prefill — attention of a chunk of new prompt tokens over the
+ * paged cache ("PagedAttention and vLLM Architecture: Virtual Memory for LLM
+ * Serving", section 3, item 1: a prompt is processed and its logical blocks
+ * are assigned physical blocks; section 2: attention reads K and V through
+ * the block table and applies softmax to the scaled dot products; the
+ * translation formula of "PagedAttention Paper Breakdown", section 2).
+ * Sequence s owns query rows q_start[s] .. q_start[s+1]-1 (n_s of them,
+ * n_s <= max_q_len); they are its newest tokens, at positions L-n_s .. L-1
+ * (L = context_lens[s], the chunk included: write the chunk's K and V with
+ * paged_kv_append first).  The row at position p attends causally to
+ * positions 0 .. p:
+ *
+ *   out[r, h, :] = sum_{i <= p} softmax_i(scale * <q[r, h, :], K_i[g, :]>) V_i[g, :]
+ *
+ * with g = h / (q_heads / kv_heads), scores, softmax and the V sum in fp32
+ * on the matrix cores.  n_s = L gives a whole prompt; n_s < L continues an
+ * earlier context (chunked prefill).
+ *
+ *   out          [total_q, q_heads, head_dim] fp32, rows of every sequence
+ *                written (NaN rows when L < n_s or L > max_context_len, or a
+ *                table entry outside the pool).
+ *   q            [total_q, q_heads, head_dim] bf16.
+ *   q_start      [num_seqs + 1] int32, device: nondecreasing, q_start[0] = 0.
+ *   block_tables, context_lens, caches: as paged_attn_decode.
+ *   max_q_len    host-side upper bound of n_s; sizes the grid.
+ * Supported: dtype BF16 (PKV_ERR_UNSUPPORTED for F32); head_dim 64 or 128;
+ * block_size 16 or 32; group size 1, 2, 4, 8 or 16.  Errors: PKV_ERR_NULL,
+ * PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ */
+PKV_API int paged_attn_prefill(float* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, const int32_t* q_start,
+                               int32_t num_seqs, int32_t max_q_len, int32_t q_heads, int32_t kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, int32_t max_context_len, float scale, int32_t dtype,
+                               void* stream);
+
+/*
  * paged_kv_copy_blocks — the block copy of copy-on-write ("PagedAttention and
  * vLLM Architecture: Virtual Memory for LLM Serving", section 3: a stream that
  * must write into a shared block first gets a fresh block holding a copy of

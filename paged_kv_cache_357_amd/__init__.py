@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     decode,
     load_library,
     plan,
+    prefill,
     slot_mapping,
     status_str,
     workspace_size,

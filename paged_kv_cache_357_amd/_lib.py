@@ -37,6 +37,7 @@ SIGNATURES = {
     "paged_attn_decode_workspace_size": (_c_sz, [_c_i32] * 8),
     "paged_status_str": (ctypes.c_char_p, [_c_int]),
     "paged_kv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp] + [_c_i32] * 6 + [_vp]),
+    "paged_attn_prefill": (_c_int, [_vp] * 7 + [_c_i32] * 9 + [_c_f, _c_i32, _vp]),
     "pkv_bm_create": (_vp, [_c_i32] * 3),
     "pkv_bm_destroy": (None, [_vp]),
     "pkv_bm_add_sequence": (_c_int, [_vp, _i32p]),
@@ -173,6 +174,32 @@ def copy_blocks(k_cache, v_cache, src, dst) -> None:
     _check("paged_kv_copy_blocks", lib.paged_kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src), _ptr(dst),
                                                             src.numel(), NB, B, Hkv, D, _DTYPES[k_cache.dtype],
                                                             _stream(dev)))
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, q_start, scale, max_q_len, max_context_len,
+            out=None) -> torch.Tensor:
+    """Causal attention of new prompt rows over the paged cache; returns out
+    [total_q, Hq, D] fp32."""
+    lib = load_library()
+    total, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    S, MB = block_tables.shape
+    _require(D2 == D and v_cache.shape == k_cache.shape, "q and caches disagree")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "mixed dtypes")
+    _require(q.dtype in _DTYPES, f"unsupported dtype {q.dtype}")
+    _require(context_lens.shape == (S,) and q_start.shape == (S + 1,), "context_lens [S], q_start [S+1]")
+    _require(block_tables.dtype == context_lens.dtype == q_start.dtype == torch.int32, "int32 index tensors")
+    _require(all(t.is_contiguous() for t in (q, k_cache, v_cache, block_tables, context_lens, q_start)),
+             "tensors must be contiguous")
+    if out is None:
+        out = torch.empty((total, Hq, D), dtype=torch.float32, device=q.device)
+    _require(out.shape == (total, Hq, D) and out.dtype == torch.float32, "out must be fp32 [total_q, Hq, D]")
+    dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens, q_start)
+    _check("paged_attn_prefill", lib.paged_attn_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                        _ptr(block_tables), _ptr(context_lens), _ptr(q_start), S,
+                                                        int(max_q_len), Hq, Hkv, D, B, NB, MB, int(max_context_len),
+                                                        float(scale), _DTYPES[q.dtype], _stream(dev)))
+    return out
 
 
 class OutOfBlocksError(PagedKVError):

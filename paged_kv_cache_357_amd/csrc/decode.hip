@@ -1158,6 +1158,122 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_wide_kernel(D
   orow[d] = tn / td;
 }
 
+// ------------------------------------------------------------ prompt pass
+//
+// Causal attention of a chunk of new query tokens over their sequence's
+// cache (the chunk's own K and V already written): the token at position p
+// attends to positions 0 .. p.  One wave takes a tile of 16 query rows, the
+// (token, head) pairs of 16 / G consecutive tokens and the G query heads of
+// kv head g; the four waves of a workgroup take four consecutive tiles of
+// the same (sequence, kv head), so they read the same K and V through L2.
+// Each wave streams its sequence's 16-token chunks from position 0 to its
+// last token's position through the matrix-core core: scores K q^T, online
+// softmax per column and O^T += V^T P^T, exactly as the decode step, with the
+// mask limit taken per column (each column's own position) instead of per
+// chunk.  Tiles are dealt last-first so the longest ones start first.
+
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams a) {
+  using Core = MfmaCore<D, B, G>;
+  constexpr int ROW = Core::ROW, CW = Core::CW, QT = 16 / G;
+  __shared__ __attribute__((aligned(16))) char s_stage[kWavesPerWG][Core::kStageBytes];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int u = (int)blockIdx.x * kWavesPerWG + wave;
+  if (u >= a.n_units) return;
+  const int lane = threadIdx.x & 63;
+  const int qt = a.n_qt - 1 - u % a.n_qt;  // last tiles first
+  const int sg = u / a.n_qt;
+  const int s = sg / a.Hkv;
+  const int g = sg - s * a.Hkv;
+  const int r0 = a.q_start[s];
+  const int n = a.q_start[s + 1] - r0;
+  const int t0 = qt * QT;
+  if (t0 >= n) return;
+  const int L = a.lens[s];
+  const int cl = lane & 15, gl = lane >> 4;
+  const int t = t0 + cl / G;               // this lane's column: token t, head h of the group
+  const int h = cl % G;
+  const bool col_ok = t < n;
+  float* orow = a.out + ((size_t)(r0 + t) * a.Hq + (size_t)g * G + h) * D;
+  if (L < n || L > a.max_len || L <= 0) {   // lengths that cannot hold the chunk: NaN rows
+    if (col_ok)
+      for (int d = gl; d < D; d += 4) orow[d] = __builtin_nanf("");
+    return;
+  }
+  const int p_col = col_ok ? L - n + t : -1;              // last key this column sees
+  const int p_max = L - n + min(t0 + QT, n) - 1;          // last key of the tile
+  const int n_chunks = p_max / kChunk + 1;
+  const int n_blk = p_max / B + 1;
+  const int32_t* trow = a.tables + (size_t)s * a.MB;
+  const uint32_t rs = (uint32_t)a.Hkv * ROW;
+  const char* kbase = static_cast<const char*>(a.k) + (size_t)g * ROW;
+  const char* vbase = static_cast<const char*>(a.v) + (size_t)g * ROW;
+
+  Core core;
+  core.init(lane, rs, s_stage[wave]);
+  // q^T operand: column cl is query row r0 + t, head g * G + h.
+  {
+    const char* qsrc = static_cast<const char*>(a.q) + ((size_t)(r0 + t) * a.Hq + (size_t)g * G + h) * ROW;
+#pragma unroll
+    for (int j = 0; j < Core::KSTEPS; ++j) {
+      uint4 v4 = make_uint4(0, 0, 0, 0);
+      if (col_ok) v4 = *reinterpret_cast<const uint4*>(qsrc + 16 * (gl + 4 * j));
+      core.q[j] = __builtin_bit_cast(bf16x8, make_u32x4(v4));
+    }
+  }
+  core.reset();
+  bool bad = false;
+  int wbase = 0;
+  int tbl = load_table_window(trow, 0, n_blk, lane, a.NB, &bad);
+
+  auto issue = [&](int c, typename Core::Buf& b) {
+    const int cs = c * kChunk;
+    const int bi = cs / B;
+    if (bi - wbase >= 64) {
+      wbase += 64;
+      tbl = load_table_window(trow, wbase, n_blk, lane, a.NB, &bad);
+    }
+    const int phys = __builtin_amdgcn_readlane(tbl, bi - wbase);
+    const size_t cbase = ((size_t)phys * B + (size_t)(cs % B)) * rs;
+    const int lim = min(kChunk - 1, p_max - cs);  // last row of the chunk any column needs
+    core.issue(kbase + cbase, vbase + cbase, rs, (uint32_t)lim * rs + ROW, b);
+  };
+  auto consume = [&](int c, const typename Core::Buf& b) { core.consume(p_col - c * kChunk, a.scale_log2, b); };
+  typename Core::Buf ba, bb;
+  issue(0, ba);
+  int c = 0;
+  for (; c + 2 < n_chunks; c += 2) {
+    issue(c + 1, bb);
+    consume(c, ba);
+    issue(c + 2, ba);
+    consume(c + 1, bb);
+  }
+  if (c + 1 < n_chunks) {
+    issue(c + 1, bb);
+    consume(c, ba);
+    consume(c + 1, bb);
+  } else {
+    consume(c, ba);
+  }
+
+  // Lane (gl, cl) holds columns CW * (4 gl + r) + dt of its row (as in the
+  // decode step); the four lane groups share the running max, their sums add.
+  float lt = core.l_run + __shfl_xor(core.l_run, 16);
+  lt += __shfl_xor(lt, 32);
+  if (!col_ok) return;
+  const int col0 = 4 * CW * gl;
+  const float nan = __builtin_nanf("");
+  float4* dst = reinterpret_cast<float4*>(orow + col0);
+#pragma unroll
+  for (int e = 0; e < 4 * CW; e += 4) {
+    float v4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4[i] = core.acc[(e + i) % CW][(e + i) / CW];
+    dst[e / 4] = bad ? make_float4(nan, nan, nan, nan)
+                     : make_float4(v4[0] / lt, v4[1] / lt, v4[2] / lt, v4[3] / lt);
+  }
+}
+
 // ------------------------------------------------------------------ launch
 
 template <int DT, int D, int B, int G>
@@ -1209,6 +1325,28 @@ hipError_t launch_d(const DecodeParams& p, int head_dim, int block_size, int gro
 }
 
 }  // namespace
+
+template <int D, int B>
+hipError_t launch_prefill_g(const PrefillParams& p, int group, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.n_units + kWavesPerWG - 1) / kWavesPerWG));
+  switch (group) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, B, 1>), grid, dim3(kThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, B, 2>), grid, dim3(kThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, B, 4>), grid, dim3(kThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, B, 8>), grid, dim3(kThreads), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<D, B, 16>), grid, dim3(kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int block_size, int group, hipStream_t stream) {
+  if (p.n_units == 0) return hipSuccess;
+  if (head_dim == 128) {
+    return block_size == 16 ? launch_prefill_g<128, 16>(p, group, stream) : launch_prefill_g<128, 32>(p, group, stream);
+  }
+  return block_size == 16 ? launch_prefill_g<64, 16>(p, group, stream) : launch_prefill_g<64, 32>(p, group, stream);
+}
 
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int block_size, int group,
                                     hipStream_t stream) {

@@ -219,6 +219,50 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_attn_prefill(float* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, const int32_t* q_start,
+                       int32_t num_seqs, int32_t max_q_len, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       float scale, int32_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || max_q_len < 0 || q_heads <= 0 || kv_heads <= 0 || max_context_len < 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || block_size <= 0 || head_dim <= 0)
+    return PKV_ERR_SHAPE;
+  if (q_heads % kv_heads) return PKV_ERR_SHAPE;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+  if (max_q_len > max_context_len) return PKV_ERR_SHAPE;
+  const int group = q_heads / kv_heads;
+  if (dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;  // the matrix-core path takes bf16
+  if (!(group == 1 || group == 2 || group == 4 || group == 8 || group == 16)) return PKV_ERR_UNSUPPORTED;
+  if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
+  if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
+  const int tile = 16 / group;
+  const long long n_qt = ((long long)max_q_len + tile - 1) / tile;
+  const long long units = (long long)num_seqs * kv_heads * n_qt;
+  if (units > 0x7fffffffLL - 4) return PKV_ERR_UNSUPPORTED;
+  if (units == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !q_start) return PKV_ERR_NULL;
+  pkv::PrefillParams p;
+  p.out = out;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.tables = block_tables;
+  p.lens = context_lens;
+  p.q_start = q_start;
+  p.S = num_seqs;
+  p.Hq = q_heads;
+  p.Hkv = kv_heads;
+  p.NB = num_blocks;
+  p.MB = max_blocks_per_seq;
+  p.max_len = max_context_len;
+  p.n_qt = (int)n_qt;
+  p.n_units = (int)units;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  const hipError_t e = pkv::launch_prefill(p, head_dim, block_size, group, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t max_context_len, int32_t dtype, int32_t partition_size,
                            int32_t* resolved_partition_size, int32_t* num_partitions) {

@@ -80,6 +80,23 @@ struct DecodeParams {
   float scale_log2;       // scale * log2(e): scores live in the base-2 domain
 };
 
+// Arguments of the prompt (prefill) attention kernel.
+struct PrefillParams {
+  float* out;               // [total_q, Hq, D]
+  const void* q;            // [total_q, Hq, D]
+  const void* k;            // [NB, B, Hkv, D]
+  const void* v;            // [NB, B, Hkv, D]
+  const int32_t* tables;    // [S, MB]
+  const int32_t* lens;      // [S] tokens held, the new chunk included
+  const int32_t* q_start;   // [S + 1] rows of sequence s: q_start[s] .. q_start[s+1]-1
+  int32_t S, Hq, Hkv, NB, MB, max_len;
+  int32_t n_qt;             // query tiles per (sequence, kv head): ceil(max_q_len / tile tokens)
+  int32_t n_units;          // S * Hkv * n_qt waves
+  float scale_log2;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int block_size, int group, hipStream_t stream);
+
 // Stage 1 / stage 2 launchers (decode.hip).  Return hipSuccess or the launch error.
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int block_size,
                                     int group, hipStream_t stream);

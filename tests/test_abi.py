@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -117,6 +117,14 @@ def test_append_and_slot_mapping_reject(lib):
     assert lib.paged_kv_slot_mapping(None, None, None, 4, 3, 16, 32, None) == -1
     assert lib.paged_kv_slot_mapping(fake, fake, fake, 4, 3, 16, 0x7fffffff, None) == -2
     assert lib.paged_kv_slot_mapping(None, None, None, 0, 3, 16, 32, None) == 0
+    f = lib.paged_attn_prefill
+    assert f(*([None] * 7 + [2, 16, 4, 4, 128, 16, 32, 8, 64]), ctypes.c_float(0.1), 1, None) == -1
+    assert f(*([fake] * 7 + [2, 16, 4, 4, 128, 16, 32, 8, 64]), ctypes.c_float(0.1), 0, None) == -4  # f32
+    assert f(*([fake] * 7 + [2, 16, 4, 4, 96, 16, 32, 8, 64]), ctypes.c_float(0.1), 1, None) == -4   # head_dim
+    assert f(*([fake] * 7 + [2, 16, 4, 3, 128, 16, 32, 8, 64]), ctypes.c_float(0.1), 1, None) == -2  # Hq % Hkv
+    assert f(*([fake] * 7 + [2, 16, 4, 4, 128, 16, 32, 8, 200]), ctypes.c_float(0.1), 1, None) == -2 # > MB * B
+    assert f(*([fake] * 7 + [2, 80, 4, 4, 128, 16, 32, 8, 64]), ctypes.c_float(0.1), 1, None) == -2  # max_q > max_len
+    assert f(*([None] * 7 + [0, 16, 4, 4, 128, 16, 32, 8, 64]), ctypes.c_float(0.1), 1, None) == 0   # nothing to do
     f = lib.paged_kv_copy_blocks
     assert f(None, None, None, None, 3, 32, 16, 4, 64, 0, None) == -1
     assert f(fake, fake, fake, fake, 3, 32, 16, 4, 64, 5, None) == -3
