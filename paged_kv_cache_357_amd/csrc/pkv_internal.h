@@ -90,8 +90,8 @@ struct PrefillParams {
   const int32_t* lens;      // [S] tokens held, the new chunk included
   const int32_t* q_start;   // [S + 1] rows of sequence s: q_start[s] .. q_start[s+1]-1
   int32_t S, Hq, Hkv, NB, MB, max_len;
-  int32_t n_qt;             // query tiles per (sequence, kv head): ceil(max_q_len / tile tokens)
-  int32_t n_units;          // S * Hkv * n_qt waves
+  int32_t n_qt;             // workgroup tiles per (sequence, kv head): ceil(max_q_len / tile tokens)
+  int32_t n_units;          // S * Hkv * n_qt workgroups
   float scale_log2;
 };
 
