@@ -28,7 +28,7 @@ HOST_CXX = os.environ.get("CXX", "g++")
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden", "-I", os.path.join(ROOT, "include")]
 
 LIBS = {
-    "libpagedkv.so": ["pagedkv_api.hip", "decode.hip", "append.hip", "block_manager.cpp"],
+    "libpagedkv.so": ["pagedkv_api.hip", "decode.hip", "prefill.hip", "append.hip", "block_manager.cpp"],
     "libpkv_probes.so": ["bench_probes.hip"],
 }
 

@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "pkv_internal.h"
+#include "pkv_ops.h"
 
 namespace pkv {
 namespace {

@@ -9,6 +9,7 @@
 
 #include "pagedkv.h"
 #include "pkv_internal.h"
+#include "pkv_ops.h"
 
 namespace {
 

@@ -1,0 +1,328 @@
+// Prompt (prefill) attention over the paged KV cache for gfx950.
+//
+// "PagedAttention and vLLM Architecture: Virtual Memory for LLM Serving",
+// section 3, item 1: a prompt is processed and its logical blocks are
+// assigned physical blocks; section 2: attention reads K and V through the
+// block table and applies softmax to the scaled dot products.  Positions
+// follow the translation formula of "PagedAttention Paper Breakdown",
+// section 2.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "pkv_internal.h"
+#include "pkv_ops.h"
+
+namespace pkv {
+namespace {
+
+constexpr float kNegBig = -1.0e30f;
+constexpr int kThreads = kWavesPerWG * 64;
+// Fourth word of a raw buffer resource on gfx9-family parts (gfx950).
+constexpr int kBufferConfig = 0x00020000;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ u32x4 make_u32x4(const uint4& t) { return u32x4{t.x, t.y, t.z, t.w}; }
+
+// Two floats rounded to bf16 (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ------------------------------------------------------------ prompt pass
+//
+// Causal attention of a chunk of new query tokens over their sequence's
+// cache (the chunk's own K and V already written): the token at position p
+// attends to positions 0 .. p.  A wave takes a tile of 16 query columns,
+// the (token, head) pairs of QT = 16 / G consecutive tokens and the G query
+// heads of kv head g; a workgroup takes four consecutive tiles of one
+// (sequence, kv head).  The workgroup streams the sequence's 16-token chunks
+// from position 0 to its last token's position: all 256 threads load a
+// chunk's K and V rows once into a double-buffered LDS tile (one barrier
+// per chunk), and each wave runs the decode step's matrix-core math on its
+// columns: scores K q^T, an online softmax per column with the mask limit
+// at the column's own position, and O^T += V^T P^T with the weights carried
+// as two bf16 parts.  A wave past its own last position only helps load.
+// Workgroup tiles are dealt last-first so the longest start first.
+
+// Headroom (base 2) a weight may reach before the prompt pass moves its
+// softmax reference.
+constexpr float kLazy = 8.0f;
+
+// Three waves per SIMD: with that register budget the accumulators stay in
+// VGPRs (left to itself the compiler parks them in AGPRs and pays a copy
+// each way around every rescale, about 15% of the pass).
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(PrefillParams a) {
+  constexpr int ROW = D * 2;            // bytes of one token row of one kv head
+  constexpr int LPR = ROW / 16;         // 16-byte pieces per row
+  constexpr int KSTEPS = D / 32;
+  constexpr int CW = D / 16;            // bf16 per lane of a V row = output tiles
+  constexpr int QT = 16 / G;            // tokens per wave tile
+  constexpr int STEP = 2 * kChunk;      // keys per step: two 16-key halves
+  constexpr int TILE = STEP * ROW;      // bytes of one step of K (or V)
+  static_assert(kThreads >= kChunk * LPR, "one load per thread covers a half");
+  using VRow = typename std::conditional<CW == 8, u32x4, u32x2>::type;
+  __shared__ __attribute__((aligned(16))) char s_k[2][TILE];
+  __shared__ __attribute__((aligned(16))) char s_v[2][TILE];
+
+  const int u = (int)blockIdx.x;
+  const int wgt = a.n_qt - 1 - u % a.n_qt;  // last tiles first
+  const int sg = u / a.n_qt;
+  const int s = sg / a.Hkv;
+  const int g = sg - s * a.Hkv;
+  const int r0 = a.q_start[s];
+  const int n = a.q_start[s + 1] - r0;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int wg_t0 = wgt * kWavesPerWG * QT;
+  if (wg_t0 >= n) return;  // uniform over the workgroup
+  const int L = a.lens[s];
+  const int cl = lane & 15, gl = lane >> 4;
+  const int t0 = wg_t0 + wave * QT;
+  const int t = t0 + cl / G;               // this lane's column: token t, head h of the group
+  const int h = cl % G;
+  const bool col_ok = t < n;
+  float* orow = a.out + ((size_t)(r0 + t) * a.Hq + (size_t)g * G + h) * D;
+  if (L < n || L > a.max_len) {            // lengths that cannot hold the chunk: NaN rows
+    if (col_ok)
+      for (int d = gl; d < D; d += 4) orow[d] = __builtin_nanf("");
+    return;
+  }
+  const int p_col = col_ok ? L - n + t : -1;                         // last key this column sees
+  const int p_wave = t0 < n ? L - n + min(t0 + QT, n) - 1 : -1;      // last key of this wave
+  const int p_wg = L - n + min(wg_t0 + kWavesPerWG * QT, n) - 1;     // last key of the workgroup
+  const int n_steps = p_wg / STEP + 1;
+  const int32_t* trow = a.tables + (size_t)s * a.MB;
+  const uint32_t rs = (uint32_t)a.Hkv * ROW;
+  const char* kbase = static_cast<const char*>(a.k) + (size_t)g * ROW;
+  const char* vbase = static_cast<const char*>(a.v) + (size_t)g * ROW;
+
+  // q^T operand: column cl is query row r0 + t, head g * G + h.
+  bf16x8 q[KSTEPS];
+  {
+    const char* qsrc = static_cast<const char*>(a.q) + ((size_t)(r0 + t) * a.Hq + (size_t)g * G + h) * ROW;
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+      uint4 v4 = make_uint4(0, 0, 0, 0);
+      if (col_ok) v4 = *reinterpret_cast<const uint4*>(qsrc + 16 * (gl + 4 * j));
+      q[j] = __builtin_bit_cast(bf16x8, make_u32x4(v4));
+    }
+  }
+  f32x4 acc[CW];
+#pragma unroll
+  for (int dt = 0; dt < CW; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = kNegBig, l_run = 0.0f;
+
+  // Step loads: for each 16-key half, thread tid moves 16 bytes (piece
+  // tid % LPR of row tid / LPR) of K and of V.  Halves past the last needed
+  // key go through zero-size resources (no data moves), so every step
+  // issues the same loads and each wait is exact.
+  const int lr = tid / LPR, lc = tid % LPR;
+  const bool loader = lr < kChunk;
+  bool bad = false;
+  auto load = [&](int c, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int cs = c * STEP + half * kChunk;
+      const bool live = cs <= p_wg;
+      int blk = trow[(live ? cs : 0) / B];
+      if (blk < 0 || blk >= a.NB) {  // never dereferenced; the rows become NaN
+        if (live) bad = true;
+        blk = 0;
+      }
+      const size_t cbase = ((size_t)blk * B + (size_t)(cs % B)) * rs;
+      const int lim = min(kChunk - 1, p_wg - cs);  // rows past the last needed key read as zero
+      const uint32_t nbytes = live ? (uint32_t)lim * rs + ROW : 0u;
+      const __amdgpu_buffer_rsrc_t kres =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + cbase), 0, (int)nbytes, kBufferConfig);
+      const __amdgpu_buffer_rsrc_t vres =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + cbase), 0, (int)nbytes, kBufferConfig);
+      const int off = loader ? (int)((uint32_t)lr * rs) + lc * 16 : (int)nbytes;  // idle threads load nothing
+      kr[half] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, off, 0, 0));
+      vr[half] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0));
+    }
+  };
+  auto store = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
+    if (!loader) return;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int r = half * kChunk + lr;
+      // K: piece lc of row r at (lc ^ (r mod LPR)), so the operand reads
+      // (16 rows at one piece) fall in distinct banks.
+      *reinterpret_cast<u32x4*>(s_k[buf] + r * ROW + ((lc ^ (r % LPR)) * 16)) = kr[half];
+      *reinterpret_cast<u32x4*>(s_v[buf] + r * ROW + lc * 16) = vr[half];
+    }
+  };
+
+  // One 32-key step for this wave's 16 columns.  Lane (gl, cl) ends the
+  // score products holding keys 4 gl + r (first half) and 16 + 4 gl + r
+  // (second half), r = 0..3, of column cl.  The V product contracts over 32
+  // keys with one 16x16x32 product per output tile; its k index order is
+  // the same for both operands (k slot 8 gl + i is key 4 gl + i for i < 4,
+  // 16 + 4 gl + i - 4 after), so the lane's eight weights are its B operand
+  // as they stand.
+  auto compute = [&](int c, int buf) {
+    const int cs = c * STEP;
+    const int lim = p_col - cs;
+    f32x4 sc[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      sc[half] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int r = half * kChunk + cl;
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        const int pc = (gl + 4 * j) ^ (r % LPR);
+        const u32x4 k = *reinterpret_cast<const u32x4*>(s_k[buf] + r * ROW + pc * 16);
+        sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), q[j], sc[half], 0, 0, 0);
+      }
+    }
+    VRow vrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (i < 4 ? 0 : kChunk) + 4 * gl + (i & 3);
+      vrow[i] = *reinterpret_cast<const VRow*>(s_v[buf] + r * ROW + cl * (2 * CW));
+    }
+
+    // Online softmax with a lazily moved reference: the running reference
+    // m_run follows a column's maximum only when the maximum exceeds it by
+    // more than kLazy (base 2), so weights stay below 2^kLazy and the
+    // accumulator is rescaled rarely.  Any reference gives the same
+    // softmax; only rounding depends on it, and it depends on the data
+    // alone, so results stay deterministic.
+    float x[8];
+    float mx = kNegBig;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = (i < 4 ? 0 : kChunk) + 4 * gl + (i & 3);
+      x[i] = (key <= lim) ? sc[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool move = mx > m_run + kLazy;
+    if (__any(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < CW; ++dt) acc[dt] *= alpha;
+    }
+    float pw[8];
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pw[i] = fast_exp2(x[i] - m_run);
+      ps += pw[i];
+    }
+    l_run += ps;
+
+    // P^T operand, high (truncated) and low (rounded rest) bf16 parts.
+    uint32_t hb[8];
+    float res[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      hb[i] = __float_as_uint(pw[i]) & 0xffff0000u;
+      res[i] = pw[i] - __uint_as_float(hb[i]);
+    }
+    const bf16x8 phi = __builtin_bit_cast(
+        bf16x8, u32x4{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3], (hb[4] >> 16) | hb[5], (hb[6] >> 16) | hb[7]});
+    const bf16x8 plo = __builtin_bit_cast(
+        bf16x8, u32x4{pack_bf16_rne(res[0], res[1]), pack_bf16_rne(res[2], res[3]), pack_bf16_rne(res[4], res[5]),
+                      pack_bf16_rne(res[6], res[7])});
+#pragma unroll
+    for (int dt = 0; dt < CW; ++dt) {
+      // element dt of the eight key rows, in k slot order
+      uint32_t e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t wd = vrow[i][dt / 2];
+        e[i] = (dt % 2 == 0) ? (wd & 0xffffu) : (wd >> 16);
+      }
+      const bf16x8 vt = __builtin_bit_cast(
+          bf16x8, u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)});
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo, acc[dt], 0, 0, 0);
+    }
+  };
+
+  // Step loop: the next PD steps are loaded ahead into registers; step c is
+  // computed from one LDS buffer while step c+1 goes into the other, one
+  // barrier per step.  Slot k of the register ring holds steps k, k+PD, ..
+  // (Deeper prefetch measured no faster: the pass is bound by the wave's
+  // own instruction chain, not by load latency.)
+  constexpr int PD = 1;
+  u32x4 kr[PD][2], vr[PD][2];
+#pragma unroll
+  for (int k = 0; k < PD; ++k) load(k, kr[k], vr[k]);
+  store(0, kr[0], vr[0]);
+  __syncthreads();
+  for (int c0 = 0; c0 < n_steps; c0 += PD) {
+#pragma unroll
+    for (int k = 0; k < PD; ++k) {
+      const int c = c0 + k;
+      if (c >= n_steps) break;  // uniform over the workgroup
+      load(c + PD, kr[k], vr[k]);  // slot k is free: step c went to LDS one step ago
+      if (c * STEP <= p_wave) compute(c, c & 1);
+      if (c + 1 < n_steps) store((c + 1) & 1, kr[(k + 1) % PD], vr[(k + 1) % PD]);
+      __syncthreads();
+    }
+  }
+  bad = __syncthreads_or(bad);
+
+  // Lane (gl, cl) holds output columns CW * (4 gl + r) + dt of its row; the
+  // four lane groups share the running reference, their sums add.
+  float lt = l_run + __shfl_xor(l_run, 16);
+  lt += __shfl_xor(lt, 32);
+  if (!col_ok) return;
+  const int col0 = 4 * CW * gl;
+  const float nan = __builtin_nanf("");
+  float4* dst = reinterpret_cast<float4*>(orow + col0);
+#pragma unroll
+  for (int e = 0; e < 4 * CW; e += 4) {
+    float v4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4[i] = acc[(e + i) % CW][(e + i) / CW];
+    dst[e / 4] = bad ? make_float4(nan, nan, nan, nan)
+                     : make_float4(v4[0] / lt, v4[1] / lt, v4[2] / lt, v4[3] / lt);
+  }
+}
+
+}  // namespace
+
+template <int D, int B>
+hipError_t launch_prefill_g(const PrefillParams& p, int group, hipStream_t stream) {
+  const dim3 grid((unsigned)p.n_units);  // one workgroup per (sequence, kv head, tile of four wave tiles)
+  switch (group) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, B, 1>), grid, dim3(kThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, B, 2>), grid, dim3(kThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, B, 4>), grid, dim3(kThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, B, 8>), grid, dim3(kThreads), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<D, B, 16>), grid, dim3(kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int block_size, int group, hipStream_t stream) {
+  if (p.n_units == 0) return hipSuccess;
+  if (head_dim == 128) {
+    return block_size == 16 ? launch_prefill_g<128, 16>(p, group, stream) : launch_prefill_g<128, 32>(p, group, stream);
+  }
+  return block_size == 16 ? launch_prefill_g<64, 16>(p, group, stream) : launch_prefill_g<64, 32>(p, group, stream);
+}
+
+}  // namespace pkv
