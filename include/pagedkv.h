@@ -335,6 +335,10 @@ PKV_API int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* sr
  *                       ready to upload for paged_attn_decode.
  * pkv_bm_ref_count      sequences holding a block.
  * pkv_bm_free_blocks    blocks in the free pool (-1 for a NULL manager).
+ * pkv_bm_usage          blocks in use, slots of those blocks holding a token (a block
+ *                       shared by several sequences counted once), live sequences and
+ *                       tokens they hold (shared tokens counted per sequence): the
+ *                       internal fragmentation of the pool is 1 - filled / (used * B).
  */
 typedef struct pkv_block_manager pkv_block_manager;
 PKV_API pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq);
@@ -352,6 +356,8 @@ PKV_API int pkv_bm_tables(const pkv_block_manager* m, const int32_t* seqs, int32
                           int32_t max_blocks_per_seq, int32_t fill, int32_t* lens);
 PKV_API int pkv_bm_ref_count(const pkv_block_manager* m, int32_t block, int32_t* ref);
 PKV_API int32_t pkv_bm_free_blocks(const pkv_block_manager* m);
+PKV_API int pkv_bm_usage(const pkv_block_manager* m, int64_t* used_blocks, int64_t* filled_slots,
+                         int64_t* live_seqs, int64_t* held_tokens);
 
 /* paged_status_str — a static, human-readable name for a status code. */
 PKV_API const char* paged_status_str(int status);

@@ -49,6 +49,7 @@ SIGNATURES = {
     "pkv_bm_tables": (_c_int, [_vp, _i32p, _c_i32, _i32p, _c_i32, _c_i32, _i32p]),
     "pkv_bm_ref_count": (_c_int, [_vp, _c_i32, _i32p]),
     "pkv_bm_free_blocks": (ctypes.c_int32, [_vp]),
+    "pkv_bm_usage": (_c_int, [_vp] + [ctypes.POINTER(ctypes.c_int64)] * 4),
 }
 
 PKV_ERR_OUT_OF_BLOCKS = -7
@@ -305,6 +306,12 @@ class BlockManager:
 
     def free_blocks(self):
         return int(self.lib.pkv_bm_free_blocks(self.h))
+
+    def usage(self):
+        """(used blocks, filled slots, live sequences, held tokens)."""
+        v = [ctypes.c_int64() for _ in range(4)]
+        self._st("pkv_bm_usage", self.lib.pkv_bm_usage(self.h, *[ctypes.byref(x) for x in v]))
+        return tuple(int(x.value) for x in v)
 
     def live(self):
         return sorted(self._live)

@@ -246,4 +246,31 @@ int pkv_bm_ref_count(const pkv_block_manager* m, int32_t block, int32_t* ref) {
 
 int32_t pkv_bm_free_blocks(const pkv_block_manager* m) { return m ? m->pool.count() : -1; }
 
+int pkv_bm_usage(const pkv_block_manager* m, int64_t* used_blocks, int64_t* filled_slots, int64_t* live_seqs,
+                 int64_t* held_tokens) {
+  if (!m || !used_blocks || !filled_slots || !live_seqs || !held_tokens) return PKV_ERR_NULL;
+  // A block's filled slots are those of any sequence holding it: sharers hold
+  // identical prefixes (a write into a shared block first makes a copy).
+  std::vector<int32_t> fill((size_t)m->num_blocks, 0);
+  int64_t live = 0, held = 0;
+  for (const Sequence& q : m->seqs) {
+    if (!q.live) continue;
+    ++live;
+    held += q.len;
+    for (size_t b = 0; b < q.blocks.size(); ++b) {
+      const int64_t f = q.len - (int64_t)b * m->block_size;
+      const int32_t fb = (int32_t)(f < m->block_size ? f : m->block_size);
+      int32_t& slot = fill[(size_t)q.blocks[b]];
+      if (fb > slot) slot = fb;
+    }
+  }
+  int64_t filled = 0;
+  for (int32_t f : fill) filled += f;
+  *used_blocks = m->num_blocks - m->pool.count();
+  *filled_slots = filled;
+  *live_seqs = live;
+  *held_tokens = held;
+  return PKV_OK;
+}
+
 }  // extern "C"
