@@ -72,6 +72,8 @@ def parse():
                     help="also time this many single decode launches after a 1 GiB cache flush each")
     ap.add_argument("--cow-pairs", type=int, default=2048,
                     help="block pairs in the copy-on-write block copy timed after the step (0 = skip)")
+    ap.add_argument("--swap-blocks", type=int, default=512,
+                    help="blocks swapped out to pinned host memory and back after the step (0 = skip)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prompt-pass (prefill) attention timed after the step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -404,6 +406,41 @@ def main():
                                 "bytes_moved": moved, "ms": cms, "GBps": moved / (cms / 1e3) / 1e9,
                                 "frac_of_hbm_peak": moved / (cms / 1e3) / 1e9 / HBM_PEAK_GBS}
         del ck, cv
+
+    if args.swap_blocks > 0:
+        # Swap scattered pool blocks out to pinned host memory and back into
+        # the same blocks (the pool ends unchanged): PCIe-bound copies.
+        n = min(args.swap_blocks, w.num_blocks)
+        ids = np.random.default_rng(357200).permutation(w.num_blocks)[:n].astype(np.int32)
+        shape = (n, w.block_size, w.kv_heads, w.head_dim)
+        hk = torch.empty(shape, dtype=kc.dtype, pin_memory=True)
+        hv = torch.empty(shape, dtype=kc.dtype, pin_memory=True)
+        dt = pk.DTYPE_BF16 if kc.dtype == torch.bfloat16 else pk.DTYPE_F32
+        staging = torch.empty(pk.swap_staging_bytes(n, w.block_size, w.kv_heads, w.head_dim, dt),
+                              dtype=torch.uint8, device=dev)
+        moved = 2 * n * w.block_size * w.kv_heads * w.head_dim * kc.element_size()  # K and V
+        runs = 1 + int(np.count_nonzero(np.diff(ids) != 1))
+        extra["swap"] = {"blocks": n, "bytes_per_direction": moved}
+        for label, st in (("staged", staging), ("per_run", None)):
+            pk.swap_out(kc, vc, ids, hk, hv, staging=st)
+            pk.swap_in(kc, vc, ids, hk, hv, staging=st)
+            torch.cuda.synchronize()
+            sev = HipEvents(4 * 5, stream_ptr)
+            for i in range(5):
+                sev.record(4 * i)
+                pk.swap_out(kc, vc, ids, hk, hv, staging=st)
+                sev.record(4 * i + 1)
+                sev.record(4 * i + 2)
+                pk.swap_in(kc, vc, ids, hk, hv, staging=st)
+                sev.record(4 * i + 3)
+            torch.cuda.synchronize()
+            out_ms = float(np.median([sev.ms(4 * i, 4 * i + 1) for i in range(5)]))
+            in_ms = float(np.median([sev.ms(4 * i + 2, 4 * i + 3) for i in range(5)]))
+            sev.close()
+            extra["swap"][label] = {"copies_per_direction": 2 if st is not None else 2 * runs,
+                                    "out_ms": out_ms, "in_ms": in_ms,
+                                    "out_GBps": moved / (out_ms / 1e3) / 1e9, "in_GBps": moved / (in_ms / 1e3) / 1e9}
+        del hk, hv, staging
 
     if not args.no_prefill:
         from workloads import make_workload, normal_storage

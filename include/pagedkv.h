@@ -295,6 +295,37 @@ PKV_API int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* sr
                                  int32_t head_dim, int32_t dtype, void* stream);
 
 /*
+ * paged_kv_swap_out / paged_kv_swap_in — move whole blocks between the device
+ * pool and host memory ("PagedAttention Paper Breakdown", Engineering
+ * Limitations: under memory pressure blocks are swapped between CPU and GPU
+ * over PCIe).  Entry i of `blocks` (a HOST array of n_blocks ids in
+ * [0, num_blocks)) pairs device block blocks[i] with host slot i:
+ *   swap_out: host_k[i] <- k_cache[blocks[i]], host_v[i] <- v_cache[blocks[i]];
+ *   swap_in:  k_cache[blocks[i]] <- host_k[i], v_cache[blocks[i]] <- host_v[i].
+ * host_k, host_v: [n_blocks, block_size, kv_heads, head_dim] of dtype in host
+ * memory allocated pinned (hipHostMalloc or an equivalent pinned allocation),
+ * owned by the caller.  With a device `staging` area of at least
+ * paged_kv_swap_staging_bytes(n_blocks, ...) bytes, the ids are copied into
+ * it, a kernel gathers the blocks into contiguous K and V runs there (or
+ * scatters them back) and one copy per cache crosses PCIe; with staging NULL
+ * (or too small) runs of consecutive ids become one copy each.  Everything
+ * is enqueued on `stream` (hipMemcpyAsync), so the caller synchronises before
+ * reading host data (swap_out) or reusing host data or staging (swap_in).
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (an id outside the pool), PKV_ERR_DTYPE,
+ * PKV_ERR_HIP; n_blocks == 0 enqueues nothing.
+ */
+PKV_API int paged_kv_swap_out(const void* k_cache, const void* v_cache, const int32_t* blocks, int32_t n_blocks,
+                              void* host_k, void* host_v, void* staging, size_t staging_bytes, int32_t num_blocks,
+                              int32_t block_size, int32_t kv_heads, int32_t head_dim, int32_t dtype, void* stream);
+PKV_API int paged_kv_swap_in(void* k_cache, void* v_cache, const int32_t* blocks, int32_t n_blocks,
+                             const void* host_k, const void* host_v, void* staging, size_t staging_bytes,
+                             int32_t num_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim,
+                             int32_t dtype, void* stream);
+/* Device staging bytes a swap of n_blocks blocks can use (0 for bad sizes). */
+PKV_API size_t paged_kv_swap_staging_bytes(int32_t n_blocks, int32_t block_size, int32_t kv_heads,
+                                           int32_t head_dim, int32_t dtype);
+
+/*
  * Block manager — host-side bookkeeping of the physical block pool
  * ("PagedAttention and vLLM Architecture: Virtual Memory for LLM Serving",
  * section 1: a pool of fixed-size blocks set up at start and a per-request
@@ -315,7 +346,8 @@ PKV_API int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* sr
  *                       (num_blocks * block_size must fit int32) or no memory.
  * pkv_bm_add_sequence   a new empty sequence; its id in *seq.
  * pkv_bm_fork           a new sequence sharing all blocks (and the length) of parent.
- * pkv_bm_free           drops a sequence; blocks no sequence holds return to the pool.
+ * pkv_bm_free           drops a sequence (also a swapped one); blocks no sequence holds
+ *                       return to the pool.
  * pkv_bm_append         reserves the slots of n_tokens new tokens of seq (positions
  *                       L .. L+n_tokens-1) in slots[n_tokens].  When the first of
  *                       them falls into a block shared with another sequence, a
@@ -333,6 +365,14 @@ PKV_API int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* sr
  * pkv_bm_tables         the rows of seqs as an [n_seqs, max_blocks_per_seq] int32
  *                       table padded with `fill`, and their lengths in lens[n_seqs],
  *                       ready to upload for paged_attn_decode.
+ * pkv_bm_swap_out       moves seq to the host side: writes its block ids (table order,
+ *                       *n_blocks of them, capacity >= that) for the caller to save
+ *                       with paged_kv_swap_out, then drops seq's hold on them (blocks
+ *                       no other sequence holds return to the pool).  A swapped
+ *                       sequence cannot append, fork or swap out until swapped in.
+ * pkv_bm_swap_in        gives a swapped seq fresh private blocks (lowest first) for
+ *                       all its tokens and writes their ids for paged_kv_swap_in;
+ *                       PKV_ERR_OUT_OF_BLOCKS when the pool cannot hold them.
  * pkv_bm_ref_count      sequences holding a block.
  * pkv_bm_free_blocks    blocks in the free pool (-1 for a NULL manager).
  * pkv_bm_usage          blocks in use, slots of those blocks holding a token (a block
@@ -354,6 +394,10 @@ PKV_API int pkv_bm_table(const pkv_block_manager* m, int32_t seq, int32_t* block
                          int32_t* n_blocks, int64_t* length);
 PKV_API int pkv_bm_tables(const pkv_block_manager* m, const int32_t* seqs, int32_t n_seqs, int32_t* tables,
                           int32_t max_blocks_per_seq, int32_t fill, int32_t* lens);
+PKV_API int pkv_bm_swap_out(pkv_block_manager* m, int32_t seq, int32_t* blocks, int32_t capacity,
+                            int32_t* n_blocks);
+PKV_API int pkv_bm_swap_in(pkv_block_manager* m, int32_t seq, int32_t* blocks, int32_t capacity,
+                           int32_t* n_blocks);
 PKV_API int pkv_bm_ref_count(const pkv_block_manager* m, int32_t block, int32_t* ref);
 PKV_API int32_t pkv_bm_free_blocks(const pkv_block_manager* m);
 PKV_API int pkv_bm_usage(const pkv_block_manager* m, int64_t* used_blocks, int64_t* filled_slots,

@@ -37,7 +37,14 @@ Readings where the pages are silent (each one is listed in the design notes):
     count reaches 0 returns to the free pool;
   * sequence ids are handed out 0, 1, 2, ... and never reused;
   * an operation that would need more free blocks than the pool holds, or a
-    table longer than max_blocks, fails and changes nothing.
+    table longer than max_blocks, fails and changes nothing;
+  * swapping ("PagedAttention Paper Breakdown", Engineering Limitations:
+    under memory pressure blocks move between CPU and GPU over PCIe): a
+    swap-out saves every block of the sequence to host memory and drops the
+    sequence's hold on them (blocks no one else holds return to the pool); a
+    swap-in gives the sequence fresh private blocks, lowest first, into
+    which the saved contents return.  A swapped sequence cannot append,
+    fork or be swapped out again until it is swapped in.
 """
 from __future__ import annotations
 
@@ -57,6 +64,7 @@ class RefBlockManager:
         self.ref = [0] * num_blocks        # [B3] reference count per physical block
         self.tables = {}                   # [B1] seq id -> list of physical block ids
         self.lens = {}                     # seq id -> tokens held
+        self.swapped = {}                  # seq id -> tokens held while on the host
         self.next_id = 0
 
     # -- the free pool ([B1]); reading: lowest-numbered free block first
@@ -88,6 +96,9 @@ class RefBlockManager:
         return child
 
     def free(self, s: int) -> None:
+        if s in self.swapped:                # a swapped sequence holds no blocks
+            del self.swapped[s]
+            return
         for b in self.tables.pop(s):
             self.ref[b] -= 1
         del self.lens[s]
@@ -127,6 +138,26 @@ class RefBlockManager:
             slots.append(table[p // self.B] * self.B + p % self.B)
             self.lens[s] = p + 1
         return slots, copies
+
+    # -- swapping
+    def swap_out(self, s: int):
+        """Blocks to save (in table order); the sequence leaves the device."""
+        blocks = self.tables.pop(s)
+        for b in blocks:
+            self.ref[b] -= 1
+        self.swapped[s] = self.lens.pop(s)
+        return blocks
+
+    def swap_in(self, s: int):
+        """Fresh blocks (in table order) that receive the saved contents."""
+        L = self.swapped[s]
+        need = -(-L // self.B)
+        if need > self.free_blocks():
+            raise OutOfBlocks()
+        del self.swapped[s]
+        self.tables[s] = [self._take_block() for _ in range(need)]
+        self.lens[s] = L
+        return list(self.tables[s])
 
     # -- views
     def table(self, s: int):

@@ -22,5 +22,8 @@ from ._lib import (  # noqa: F401
     prefill,
     slot_mapping,
     status_str,
+    swap_in,
+    swap_out,
+    swap_staging_bytes,
     workspace_size,
 )

@@ -50,6 +50,11 @@ SIGNATURES = {
     "pkv_bm_ref_count": (_c_int, [_vp, _c_i32, _i32p]),
     "pkv_bm_free_blocks": (ctypes.c_int32, [_vp]),
     "pkv_bm_usage": (_c_int, [_vp] + [ctypes.POINTER(ctypes.c_int64)] * 4),
+    "pkv_bm_swap_out": (_c_int, [_vp, _c_i32, _i32p, _c_i32, _i32p]),
+    "pkv_bm_swap_in": (_c_int, [_vp, _c_i32, _i32p, _c_i32, _i32p]),
+    "paged_kv_swap_out": (_c_int, [_vp, _vp, _i32p, _c_i32, _vp, _vp, _vp, _c_sz] + [_c_i32] * 5 + [_vp]),
+    "paged_kv_swap_in": (_c_int, [_vp, _vp, _i32p, _c_i32, _vp, _vp, _vp, _c_sz] + [_c_i32] * 5 + [_vp]),
+    "paged_kv_swap_staging_bytes": (_c_sz, [_c_i32] * 5),
 }
 
 PKV_ERR_OUT_OF_BLOCKS = -7
@@ -203,6 +208,45 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, q_start, scale, max
     return out
 
 
+def _swap(fn, k_cache, v_cache, blocks, host_k, host_v, staging):
+    import numpy as np
+    lib = load_library()
+    NB, B, Hkv, D = k_cache.shape
+    blocks = np.ascontiguousarray(blocks, dtype=np.int32)
+    n = len(blocks)
+    _require(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache and v_cache differ")
+    _require(k_cache.dtype in _DTYPES, f"unsupported dtype {k_cache.dtype}")
+    for h in (host_k, host_v):
+        _require(not h.is_cuda and h.is_pinned() and h.is_contiguous(), "host buffers must be pinned CPU tensors")
+        _require(h.dtype == k_cache.dtype and h.shape[0] >= n and tuple(h.shape[1:]) == (B, Hkv, D),
+                 "host buffers must be [>= n_blocks, B, Hkv, D] of the cache dtype")
+    dev = _dev(k_cache, v_cache)
+    if staging is not None:
+        _dev(k_cache, staging)
+    _check(fn, getattr(lib, fn)(_ptr(k_cache), _ptr(v_cache), blocks.ctypes.data_as(_i32p), n,
+                                ctypes.c_void_p(host_k.data_ptr()), ctypes.c_void_p(host_v.data_ptr()),
+                                _ptr(staging), 0 if staging is None else staging.numel() * staging.element_size(),
+                                NB, B, Hkv, D, _DTYPES[k_cache.dtype], _stream(dev)))
+
+
+def swap_staging_bytes(n_blocks, block_size, kv_heads, head_dim, dtype) -> int:
+    """Device staging bytes for a swap of n_blocks blocks."""
+    return int(load_library().paged_kv_swap_staging_bytes(n_blocks, block_size, kv_heads, head_dim, dtype))
+
+
+def swap_out(k_cache, v_cache, blocks, host_k, host_v, staging=None) -> None:
+    """Copy device blocks blocks[i] of both caches to host slot i (pinned
+    host tensors [>= n, B, Hkv, D]); asynchronous on the current stream.
+    ``staging`` (a device uint8 tensor of swap_staging_bytes) batches the
+    transfer into one copy per cache."""
+    _swap("paged_kv_swap_out", k_cache, v_cache, blocks, host_k, host_v, staging)
+
+
+def swap_in(k_cache, v_cache, blocks, host_k, host_v, staging=None) -> None:
+    """Copy host slot i of both pinned host tensors to device block blocks[i]."""
+    _swap("paged_kv_swap_in", k_cache, v_cache, blocks, host_k, host_v, staging)
+
+
 class OutOfBlocksError(PagedKVError):
     pass
 
@@ -294,6 +338,22 @@ class BlockManager:
         self._st("pkv_bm_tables", self.lib.pkv_bm_tables(self.h, _p(seqs), len(seqs), _p(t), mb, int(fill),
                                                          _p(lens)))
         return t[:len(seqs)], lens[:len(seqs)].copy()
+
+    def swap_out(self, s):
+        """Block ids (table order) to save; the sequence leaves the device."""
+        buf, nb = _i32buf(self.max_blocks), ctypes.c_int32()
+        self._st("pkv_bm_swap_out", self.lib.pkv_bm_swap_out(self.h, int(s), _p(buf), self.max_blocks,
+                                                             ctypes.byref(nb)))
+        self._live.discard(int(s))
+        return [int(x) for x in buf[:nb.value]]
+
+    def swap_in(self, s):
+        """Fresh block ids (table order) that receive the saved contents."""
+        buf, nb = _i32buf(self.max_blocks), ctypes.c_int32()
+        self._st("pkv_bm_swap_in", self.lib.pkv_bm_swap_in(self.h, int(s), _p(buf), self.max_blocks,
+                                                           ctypes.byref(nb)))
+        self._live.add(int(s))
+        return [int(x) for x in buf[:nb.value]]
 
     def ref_count(self, block):
         out = ctypes.c_int32()

@@ -124,7 +124,57 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc,
   }
 }
 
+// Swap staging: move whole blocks between the pool and a contiguous staging
+// area.  gather: staging slot i <- pool block ids[i]; otherwise pool block
+// ids[i] <- staging slot i.  Same tiling as the block copy.
+__global__ __launch_bounds__(256) void stage_blocks_kernel(char* __restrict__ pk, char* __restrict__ pv,
+                                                           char* __restrict__ sk, char* __restrict__ sv,
+                                                           const int32_t* __restrict__ ids, int NB, int vpb,
+                                                           long long block_bytes, int gather, int pair0) {
+  const int i = pair0 + (int)blockIdx.y;
+  const int b = ids[i];
+  if (b < 0 || b >= NB) return;
+  const size_t pool_off = (size_t)b * (size_t)block_bytes, stage_off = (size_t)i * (size_t)block_bytes;
+  const u32x4* fk = reinterpret_cast<const u32x4*>(gather ? pk + pool_off : sk + stage_off);
+  const u32x4* fv = reinterpret_cast<const u32x4*>(gather ? pv + pool_off : sv + stage_off);
+  u32x4* tk = reinterpret_cast<u32x4*>(gather ? sk + stage_off : pk + pool_off);
+  u32x4* tv = reinterpret_cast<u32x4*>(gather ? sv + stage_off : pv + pool_off);
+  const int base = (int)blockIdx.x * kCopyVecPerWG + (int)threadIdx.x;
+  u32x4 a[kCopyPerThread], c[kCopyPerThread];
+#pragma unroll
+  for (int k = 0; k < kCopyPerThread; ++k) {
+    const int j = base + k * 256;
+    if (j < vpb) {
+      a[k] = __builtin_nontemporal_load(fk + j);
+      c[k] = __builtin_nontemporal_load(fv + j);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kCopyPerThread; ++k) {
+    const int j = base + k * 256;
+    if (j < vpb) {
+      __builtin_nontemporal_store(a[k], tk + j);
+      __builtin_nontemporal_store(c[k], tv + j);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stage_blocks(void* pool_k, void* pool_v, void* stage_k, void* stage_v, const int32_t* ids, int n,
+                               int num_blocks, long long block_bytes, bool gather, hipStream_t stream) {
+  const int vpb = (int)(block_bytes / 16);
+  const unsigned gx = (unsigned)((vpb + kCopyVecPerWG - 1) / kCopyVecPerWG);
+  for (int p0 = 0; p0 < n; p0 += 65535) {
+    const unsigned gy = (unsigned)((n - p0) < 65535 ? (n - p0) : 65535);
+    hipLaunchKernelGGL(stage_blocks_kernel, dim3(gx, gy), dim3(256), 0, stream, static_cast<char*>(pool_k),
+                       static_cast<char*>(pool_v), static_cast<char*>(stage_k), static_cast<char*>(stage_v), ids,
+                       num_blocks, vpb, block_bytes, gather ? 1 : 0, p0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int n_pairs,
                               int num_blocks, long long block_bytes, hipStream_t stream) {

@@ -66,7 +66,8 @@ class FreePool {
 struct Sequence {
   std::vector<int32_t> blocks;  // logical block b -> physical block
   int64_t len = 0;              // tokens held
-  bool live = false;
+  bool live = false;            // on the device
+  bool swapped = false;         // saved to the host, holding no blocks
 };
 
 }  // namespace
@@ -162,6 +163,11 @@ int pkv_bm_fork(pkv_block_manager* m, int32_t parent, int32_t* child) {
 
 int pkv_bm_free(pkv_block_manager* m, int32_t seq) {
   if (!m) return PKV_ERR_NULL;
+  if (seq >= 0 && (size_t)seq < m->seqs.size() && m->seqs[(size_t)seq].swapped) {
+    m->seqs[(size_t)seq].swapped = false;  // holds no blocks
+    m->seqs[(size_t)seq].len = 0;
+    return PKV_OK;
+  }
   if (!m->valid(seq)) return PKV_ERR_BAD_SEQUENCE;
   Sequence& q = m->seqs[(size_t)seq];
   for (int32_t b : q.blocks) m->release(b);
@@ -234,6 +240,40 @@ int pkv_bm_tables(const pkv_block_manager* m, const int32_t* seqs, int32_t n_seq
     for (; j < (size_t)max_blocks_per_seq; ++j) row[j] = fill;
     lens[i] = (int32_t)q.len;
   }
+  return PKV_OK;
+}
+
+int pkv_bm_swap_out(pkv_block_manager* m, int32_t seq, int32_t* blocks, int32_t capacity, int32_t* n_blocks) {
+  if (!m || !n_blocks) return PKV_ERR_NULL;
+  if (!m->valid(seq)) return PKV_ERR_BAD_SEQUENCE;
+  Sequence& q = m->seqs[(size_t)seq];
+  *n_blocks = (int32_t)q.blocks.size();
+  if ((int32_t)q.blocks.size() > capacity) return PKV_ERR_SHAPE;
+  if (!q.blocks.empty() && !blocks) return PKV_ERR_NULL;
+  for (size_t i = 0; i < q.blocks.size(); ++i) blocks[i] = q.blocks[i];
+  for (int32_t b : q.blocks) m->release(b);
+  q.blocks.clear();
+  q.live = false;
+  q.swapped = true;
+  return PKV_OK;
+}
+
+int pkv_bm_swap_in(pkv_block_manager* m, int32_t seq, int32_t* blocks, int32_t capacity, int32_t* n_blocks) {
+  if (!m || !n_blocks) return PKV_ERR_NULL;
+  if (seq < 0 || (size_t)seq >= m->seqs.size() || !m->seqs[(size_t)seq].swapped) return PKV_ERR_BAD_SEQUENCE;
+  Sequence& q = m->seqs[(size_t)seq];
+  const int64_t need = (q.len + m->block_size - 1) / m->block_size;
+  *n_blocks = (int32_t)need;
+  if (need > capacity) return PKV_ERR_SHAPE;
+  if (need > 0 && !blocks) return PKV_ERR_NULL;
+  if (need > m->pool.count()) return PKV_ERR_OUT_OF_BLOCKS;
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t b = m->take();
+    q.blocks.push_back(b);
+    blocks[i] = b;
+  }
+  q.live = true;
+  q.swapped = false;
   return PKV_OK;
 }
 

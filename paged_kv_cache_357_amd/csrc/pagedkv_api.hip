@@ -264,6 +264,95 @@ int paged_attn_prefill(float* out, const void* q, const void* k_cache, const voi
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_kv_swap_out(const void* k_cache, const void* v_cache, const int32_t* blocks, int32_t n_blocks, void* host_k,
+                      void* host_v, void* staging, size_t staging_bytes, int32_t num_blocks, int32_t block_size,
+                      int32_t kv_heads, int32_t head_dim, int32_t dtype, void* stream);
+int paged_kv_swap_in(void* k_cache, void* v_cache, const int32_t* blocks, int32_t n_blocks, const void* host_k,
+                     const void* host_v, void* staging, size_t staging_bytes, int32_t num_blocks, int32_t block_size,
+                     int32_t kv_heads, int32_t head_dim, int32_t dtype, void* stream);
+
+size_t paged_kv_swap_staging_bytes(int32_t n_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim,
+                                   int32_t dtype);
+
+static size_t staging_need(int32_t n_blocks, size_t bb) { return round_up((size_t)n_blocks * 4, 256) + 2 * (size_t)n_blocks * bb; }
+
+static int swap_blocks(bool out, char* dev_k, char* dev_v, const int32_t* blocks, int32_t n_blocks, char* host_k,
+                char* host_v, void* staging, size_t staging_bytes, int32_t num_blocks, int32_t block_size,
+                int32_t kv_heads, int32_t head_dim, int32_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (n_blocks < 0 || num_blocks <= 0 || block_size <= 0 || kv_heads <= 0 || head_dim <= 0) return PKV_ERR_SHAPE;
+  if (n_blocks == 0) return PKV_OK;
+  if (!dev_k || !dev_v || !blocks || !host_k || !host_v) return PKV_ERR_NULL;
+  for (int32_t i = 0; i < n_blocks; ++i)
+    if (blocks[i] < 0 || blocks[i] >= num_blocks) return PKV_ERR_SHAPE;
+  const size_t bb = (size_t)block_size * kv_heads * head_dim * elt_bytes(dtype);
+  if (bb % 16 || bb > 0x7fffffffULL) return PKV_ERR_SHAPE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (staging && staging_bytes >= staging_need(n_blocks, bb)) {
+    // ids into the staging area, blocks gathered into (or scattered from)
+    // contiguous K and V runs, one DMA per cache across PCIe
+    char* st = static_cast<char*>(staging);
+    int32_t* ids = reinterpret_cast<int32_t*>(st);
+    char* st_k = st + round_up((size_t)n_blocks * 4, 256);
+    char* st_v = st_k + (size_t)n_blocks * bb;
+    const size_t bytes = (size_t)n_blocks * bb;
+    hipError_t e = hipMemcpyAsync(ids, blocks, (size_t)n_blocks * 4, hipMemcpyHostToDevice, s);
+    if (out) {
+      if (e == hipSuccess) e = pkv::launch_stage_blocks(dev_k, dev_v, st_k, st_v, ids, n_blocks, num_blocks, (long long)bb, true, s);
+      if (e == hipSuccess) e = hipMemcpyAsync(host_k, st_k, bytes, hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipMemcpyAsync(host_v, st_v, bytes, hipMemcpyDeviceToHost, s);
+    } else {
+      if (e == hipSuccess) e = hipMemcpyAsync(st_k, host_k, bytes, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipMemcpyAsync(st_v, host_v, bytes, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = pkv::launch_stage_blocks(dev_k, dev_v, st_k, st_v, ids, n_blocks, num_blocks, (long long)bb, false, s);
+    }
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  }
+  for (int32_t i = 0; i < n_blocks;) {
+    int32_t j = i + 1;  // the run blocks[i] .. blocks[j-1] is consecutive
+    while (j < n_blocks && blocks[j] == blocks[j - 1] + 1) ++j;
+    const size_t bytes = (size_t)(j - i) * bb;
+    char* d_k = dev_k + (size_t)blocks[i] * bb;
+    char* d_v = dev_v + (size_t)blocks[i] * bb;
+    char* h_k = host_k + (size_t)i * bb;
+    char* h_v = host_v + (size_t)i * bb;
+    hipError_t e;
+    if (out) {
+      e = hipMemcpyAsync(h_k, d_k, bytes, hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipMemcpyAsync(h_v, d_v, bytes, hipMemcpyDeviceToHost, s);
+    } else {
+      e = hipMemcpyAsync(d_k, h_k, bytes, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipMemcpyAsync(d_v, h_v, bytes, hipMemcpyHostToDevice, s);
+    }
+    if (e != hipSuccess) return PKV_ERR_HIP;
+    i = j;
+  }
+  return PKV_OK;
+}
+
+int paged_kv_swap_out(const void* k_cache, const void* v_cache, const int32_t* blocks, int32_t n_blocks, void* host_k,
+                      void* host_v, void* staging, size_t staging_bytes, int32_t num_blocks, int32_t block_size,
+                      int32_t kv_heads, int32_t head_dim, int32_t dtype, void* stream) {
+  return swap_blocks(true, static_cast<char*>(const_cast<void*>(k_cache)),
+                     static_cast<char*>(const_cast<void*>(v_cache)), blocks, n_blocks, static_cast<char*>(host_k),
+                     static_cast<char*>(host_v), staging, staging_bytes, num_blocks, block_size, kv_heads, head_dim,
+                     dtype, stream);
+}
+
+int paged_kv_swap_in(void* k_cache, void* v_cache, const int32_t* blocks, int32_t n_blocks, const void* host_k,
+                     const void* host_v, void* staging, size_t staging_bytes, int32_t num_blocks, int32_t block_size,
+                     int32_t kv_heads, int32_t head_dim, int32_t dtype, void* stream) {
+  return swap_blocks(false, static_cast<char*>(k_cache), static_cast<char*>(v_cache), blocks, n_blocks,
+                     static_cast<char*>(const_cast<void*>(host_k)), static_cast<char*>(const_cast<void*>(host_v)),
+                     staging, staging_bytes, num_blocks, block_size, kv_heads, head_dim, dtype, stream);
+}
+
+size_t paged_kv_swap_staging_bytes(int32_t n_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim,
+                                   int32_t dtype) {
+  if (!valid_dtype(dtype) || n_blocks < 0 || block_size <= 0 || kv_heads <= 0 || head_dim <= 0) return 0;
+  return staging_need(n_blocks, (size_t)block_size * kv_heads * head_dim * elt_bytes(dtype));
+}
+
 int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t max_context_len, int32_t dtype, int32_t partition_size,
                            int32_t* resolved_partition_size, int32_t* num_partitions) {

@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 23, names
+    assert len(names) == 28, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -125,6 +125,14 @@ def test_append_and_slot_mapping_reject(lib):
     assert f(*([fake] * 7 + [2, 16, 4, 4, 128, 16, 32, 8, 200]), ctypes.c_float(0.1), 1, None) == -2 # > MB * B
     assert f(*([fake] * 7 + [2, 80, 4, 4, 128, 16, 32, 8, 64]), ctypes.c_float(0.1), 1, None) == -2  # max_q > max_len
     assert f(*([None] * 7 + [0, 16, 4, 4, 128, 16, 32, 8, 64]), ctypes.c_float(0.1), 1, None) == 0   # nothing to do
+    blocks = (ctypes.c_int32 * 3)(0, 1, 40)
+    for f in (lib.paged_kv_swap_out, lib.paged_kv_swap_in):
+        assert f(fake, fake, blocks, 3, fake, fake, None, 0, 32, 16, 4, 64, 0, None) == -2  # block 40 outside
+        assert f(None, fake, blocks, 2, fake, fake, None, 0, 32, 16, 4, 64, 0, None) == -1
+        assert f(fake, fake, blocks, 2, fake, fake, None, 0, 32, 16, 4, 64, 9, None) == -3
+        assert f(None, None, None, 0, None, None, None, 0, 32, 16, 4, 64, 0, None) == 0    # nothing to do
+    assert lib.paged_kv_swap_staging_bytes(3, 16, 4, 64, 0) == 256 + 2 * 3 * 16 * 4 * 64 * 4
+    assert lib.paged_kv_swap_staging_bytes(3, 16, 4, 64, 7) == 0
     f = lib.paged_kv_copy_blocks
     assert f(None, None, None, None, 3, 32, 16, 4, 64, 0, None) == -1
     assert f(fake, fake, fake, fake, 3, 32, 16, 4, 64, 5, None) == -3

@@ -290,6 +290,12 @@ def _native_cls():
             except pk.OutOfBlocksError:
                 raise OutOfBlocks()
 
+        def swap_in(self, s):
+            try:
+                return super().swap_in(s)
+            except pk.OutOfBlocksError:
+                raise OutOfBlocks()
+
     return NativeBM
 
 
@@ -355,3 +361,126 @@ def test_native_manager_rejects_bad_calls():
     with pytest.raises(pk.PagedKVError):
         m.free(s)                                      # already gone
     assert lib.pkv_bm_free_blocks(None) == -1
+
+
+# ----------------------------------------------------------------- swapping
+
+def _swap_script(seed, n_ops=500):
+    rng = random.Random(seed)
+    ops = []
+    for _ in range(n_ops):
+        r = rng.random()
+        if r < 0.12:
+            ops.append(("add",))
+        elif r < 0.27:
+            ops.append(("fork", rng.random()))
+        elif r < 0.33:
+            ops.append(("free", rng.random()))
+        elif r < 0.43:
+            ops.append(("swap_out", rng.random()))
+        elif r < 0.53:
+            ops.append(("swap_in", rng.random()))
+        else:
+            ops.append(("append", rng.random(), rng.choice([1, 1, 2, 5, 16, 17, 33])))
+    return ops
+
+
+def run_swap_script(m, ops, on_event=None):
+    """Like run_script, plus swaps.  on_event(kind, s, data) sees appends
+    (slots, copies), swap-outs (blocks to save) and swap-ins (new blocks)."""
+    trace, swapped = [], []
+    for op in ops:
+        live = m.live()
+        if op[0] == "add":
+            trace.append(("add", m.add_sequence()))
+            continue
+        if op[0] == "swap_in":
+            if not swapped:
+                continue
+            s = swapped[int(op[1] * len(swapped))]
+            try:
+                blocks = m.swap_in(s)
+            except OutOfBlocks:
+                trace.append(("swap_in-fail", s))
+                continue
+            swapped.remove(s)
+            trace.append(("swap_in", s, tuple(blocks)))
+            if on_event:
+                on_event("swap_in", s, blocks)
+            continue
+        if not live:
+            continue
+        s = live[int(op[1] * len(live))]
+        if op[0] == "fork":
+            trace.append(("fork", s, m.fork(s)))
+        elif op[0] == "free":
+            m.free(s)
+            trace.append(("free", s))
+        elif op[0] == "swap_out":
+            blocks = m.swap_out(s)
+            swapped.append(s)
+            trace.append(("swap_out", s, tuple(blocks)))
+            if on_event:
+                on_event("swap_out", s, blocks)
+        else:
+            try:
+                slots, copies = m.append(s, op[2])
+                trace.append(("append", s, tuple(slots), tuple(copies)))
+                if on_event:
+                    on_event("append", s, (slots, copies))
+            except OutOfBlocks:
+                trace.append(("append-fail", s, op[2]))
+    return trace, swapped
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_swaps_preserve_content_reference(seed):
+    """Through swap-outs and swap-ins every sequence still reads its own
+    history: a swap-out saves its blocks' rows to a host dict, a swap-in
+    writes them back into the new blocks."""
+    B, NB = 8, 120
+    m = RefBlockManager(NB, B, 40)
+    pool = np.full((NB, B), -1, dtype=np.int64)
+    host, history, tag = {}, {}, [0]
+
+    def on_event(kind, s, data):
+        nonlocal pool
+        if kind == "append":
+            slots, copies = data
+            pool = copy_blocks(pool, copies)
+            flat = pool.reshape(-1)
+            for slot in slots:
+                tag[0] += 1
+                flat[slot] = tag[0]
+                history.setdefault(s, []).append(tag[0])
+        elif kind == "swap_out":
+            host[s] = pool[np.asarray(data, dtype=np.int64)].copy() if data else pool[:0].copy()
+        else:
+            pool[np.asarray(data, dtype=np.int64)] = host.pop(s)
+
+    # forks copy the parent's history
+    orig_fork = m.fork
+
+    def fork(parent):
+        c = orig_fork(parent)
+        history[c] = list(history.get(parent, []))
+        return c
+    m.fork = fork
+    run_swap_script(m, _swap_script(seed), on_event)
+    for q in m.live():
+        t = m.table(q)
+        got = [int(pool[t[i // B], i % B]) for i in range(m.length(q))]
+        assert got == history.get(q, []), q
+
+
+@pytest.mark.parametrize("seed", [5, 6, 7])
+def test_native_swaps_equal_reference(seed):
+    native = _native_cls()(100, 16, 40)
+    ref = RefBlockManager(100, 16, 40)
+    ops = _swap_script(seed)
+    ta, sa = run_swap_script(native, ops)
+    tb, sb = run_swap_script(ref, ops)
+    assert ta == tb and sa == sb
+    assert native.ref == list(ref.ref) and native.free_blocks() == ref.free_blocks()
+    for s in ref.live():
+        assert native.table(s) == ref.table(s) and native.length(s) == ref.length(s)
