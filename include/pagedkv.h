@@ -145,7 +145,8 @@ PKV_API int paged_kv_append_at(void* k_cache, void* v_cache, const void* k_new, 
  * sequence's physical blocks, all in fp32.  Two schedules split the work:
  *   - balanced (partition_size 0, some L above 512 tokens, num_seqs <= 2048):
  *     the 16-token chunks of all (sequence, kv head) pairs, laid end to end,
- *     are cut into one equal share per resident worker;
+ *     are cut into one share of equal cost per resident worker (a pair costs
+ *     its chunks plus a small charge for starting it);
  *   - partitioned (otherwise): partitions of `partition_size` tokens, one
  *     wave each.
  * Pieces of a (sequence, kv head) pair computed apart are merged by a second
@@ -229,7 +230,7 @@ PKV_API int paged_attn_decode_plan(int32_t num_seqs, int32_t q_heads, int32_t kv
  * num_seqs * q_heads * num_partitions * (head_dim + 2) * 4 bytes (each part
  * rounded up to 256).  Balanced: partial records for W worker waves (two
  * records of group-size rows each, head_dim + 2 floats per row) and
- * (num_seqs + 1) * 4 bytes of chunk prefix sums.  Host only.  Returns 0 for
+ * 2 * (num_seqs + 1) * 4 bytes of chunk and cost prefix sums.  Host only.  Returns 0 for
  * arguments the decode call would reject.
  */
 PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,

@@ -20,7 +20,8 @@
 //
 // Two schedules hand out the chunks:
 //   * balanced: all segments laid end to end, (s, g) in order, are cut into
-//     one equal share per worker wave, and the grid holds exactly as many
+//     one share of equal cost per worker wave (a segment costs its chunks
+//     plus a small charge for its start), and the grid holds exactly as many
 //     waves as the chip keeps resident, so every wave starts at once and all
 //     finish together (no tail of long units started late).  A share may
 //     begin or end inside a segment; such pieces leave partial records (at
@@ -72,6 +73,11 @@ namespace pkv {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;
+// Balanced schedule: the cost, in chunks, charged for starting a segment
+// (query rows, block-table window, piece epilogue) when the shares are cut.
+// Measured: 2 evens out shares that start many short segments (lognormal
+// GQA batch +3%), and changes nothing measurable elsewhere.
+constexpr int kSegCost = 2;
 constexpr int kThreads = kWavesPerWG * 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -780,14 +786,17 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_partitioned_kernel(Dec
 // Segment (s, g) holds n_s = ceil(L_s / 16) chunks (0 for L_s <= 0 or an
 // invalid length); segments are laid out in (s, g) order, so segment (s, g)
 // starts at chunk Hkv * C_s + g * n_s, C_s = n_0 + .. + n_{s-1}, and the
-// whole batch is T = Hkv * C_S chunks.  With W worker waves (W_eff = min(W,
-// max(1, T / kBalancedMinChunks)) of them get work), wave w takes chunks
-// [w T / W_eff, (w+1) T / W_eff).  A piece of a segment that this wave both
-// starts and ends is written directly; otherwise the wave leaves a partial
-// record in slot 0 (the piece continues a segment begun by an earlier wave)
-// or slot 1 (the piece begins a segment that a later wave continues).
+// whole batch is T = Hkv * C_S chunks.  Shares are cut in cost units: a
+// segment costs kSegCost for its start plus its n_s chunks, the batch TC
+// units, and with W worker waves (W_eff = min(W, max(1, T /
+// kBalancedMinChunks)) of them get work) wave w takes the chunks whose cost
+// positions lie in [w TC / W_eff, (w+1) TC / W_eff).  A piece of a segment
+// that this wave both starts and ends is written directly; otherwise the
+// wave leaves a partial record in slot 0 (the piece continues a segment
+// begun by an earlier wave) or slot 1 (the piece begins a segment that a
+// later wave continues).
 
-// Wave whose share contains chunk c.
+// Wave whose share contains cost position c.
 __device__ __forceinline__ long long balanced_wave_of(long long c, long long T, long long W_eff) {
   return ((c + 1) * W_eff - 1) / T;
 }
@@ -806,7 +815,9 @@ void decode_balanced_kernel(DecodeParams a) {
   __shared__ __attribute__((aligned(16))) char s_stage[kWavesPerWG][Core::kStageBytes];
   int* pref = smem;               // [S + 1] chunk prefix sums C_s
   int* slen = smem + a.S + 1;     // [S] lengths (0 for invalid ones)
+  int* pcost = smem + 2 * a.S + 1;  // [S + 1] cost prefix sums: chunks + kSegCost per non-empty sequence
   __shared__ int s_wave_sum[kWavesPerWG];
+  __shared__ int s_wave_cost[kWavesPerWG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -817,32 +828,53 @@ void decode_balanced_kernel(DecodeParams a) {
     const int per = (a.S + kThreads - 1) / kThreads;
     const int s_lo = min(a.S, tid * per);
     const int s_hi = min(a.S, s_lo + per);
-    int local = 0;
+    int local = 0, local_c = 0;
     for (int s = s_lo; s < s_hi; ++s) {
       const int L = a.lens[s];
       const int Lv = (L > 0 && L <= a.max_len) ? L : 0;
       slen[s] = Lv;
-      local += (Lv + kChunk - 1) / kChunk;
+      const int n = (Lv + kChunk - 1) / kChunk;
+      local += n;
+      local_c += n > 0 ? n + kSegCost : 0;
     }
-    int incl = local;
+    int incl = local, incl_c = local_c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
+      const int tc = __shfl_up(incl_c, off);
+      if (lane >= off) {
+        incl += t;
+        incl_c += tc;
+      }
     }
-    if (lane == 63) s_wave_sum[wave] = incl;
+    if (lane == 63) {
+      s_wave_sum[wave] = incl;
+      s_wave_cost[wave] = incl_c;
+    }
     __syncthreads();
-    int run = incl - local;
-    for (int w = 0; w < wave; ++w) run += s_wave_sum[w];
+    int run = incl - local, run_c = incl_c - local_c;
+    for (int w = 0; w < wave; ++w) {
+      run += s_wave_sum[w];
+      run_c += s_wave_cost[w];
+    }
     for (int s = s_lo; s < s_hi; ++s) {
       pref[s] = run;
-      run += (slen[s] + kChunk - 1) / kChunk;
+      pcost[s] = run_c;
+      const int n = (slen[s] + kChunk - 1) / kChunk;
+      run += n;
+      run_c += n > 0 ? n + kSegCost : 0;
     }
-    if (tid == kThreads - 1) pref[a.S] = run;
+    if (tid == kThreads - 1) {
+      pref[a.S] = run;
+      pcost[a.S] = run_c;
+    }
     __syncthreads();
   }
   if (blockIdx.x == 0)
-    for (int s = tid; s <= a.S; s += kThreads) a.ws_pref[s] = pref[s];
+    for (int s = tid; s <= a.S; s += kThreads) {
+      a.ws_pref[s] = pref[s];
+      a.ws_pref[a.S + 1 + s] = pcost[s];
+    }
 
   // Work is laid out over (sequence, head group, chunk); a head group is HG
   // adjacent kv heads.  With HG = 1 each wave is a worker; with HG = 4 the
@@ -859,8 +891,28 @@ void decode_balanced_kernel(DecodeParams a) {
   const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
   if (worker >= W_eff) return;
   const int hsub = HG == 1 ? 0 : wave;                  // head of the group this wave takes
-  const long long lo = (long long)worker * T / W_eff;
-  const long long hi = (long long)(worker + 1) * T / W_eff;
+  // Shares are equal in cost: a segment costs its chunks plus kSegCost for
+  // its start (query fetch, table window, piece write).  chunk_at maps a
+  // cost position to the first chunk at or after it.
+  const long long TC = (long long)NGR * uniform(pcost[a.S]);
+  auto chunk_at = [&](long long x) -> long long {
+    if (x >= TC) return T;
+    int sa2 = 0, sb2 = a.S;
+    while (sb2 - sa2 > 1) {
+      const int mid = (sa2 + sb2) >> 1;
+      if ((long long)NGR * uniform(pcost[mid]) <= x) sa2 = mid;
+      else sb2 = mid;
+    }
+    const int n = uniform(pref[sa2 + 1]) - uniform(pref[sa2]);
+    const long long rel = x - (long long)NGR * uniform(pcost[sa2]);
+    const long long seg = n + kSegCost;
+    const long long g2 = rel / seg;
+    const long long r = rel - g2 * seg;
+    const long long j = r < kSegCost ? 0 : r - kSegCost;
+    return (long long)NGR * uniform(pref[sa2]) + g2 * n + j;
+  };
+  const long long lo = chunk_at((long long)worker * TC / W_eff);
+  const long long hi = chunk_at((long long)(worker + 1) * TC / W_eff);
 
   // Locate the segment holding chunk lo: the last s with NGR * C_s <= lo.
   int sa = 0, sb = a.S;
@@ -1020,9 +1072,10 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(Decode
   const long long T = (long long)NGR * a.ws_pref[a.S];
   const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
   const int n = (L + kChunk - 1) / kChunk;
-  const long long base = (long long)NGR * a.ws_pref[s] + (long long)(g / HG) * n;
-  const long long w0 = balanced_wave_of(base, T, W_eff);  // first and last worker of the segment
-  const long long w1 = balanced_wave_of(base + n - 1, T, W_eff);
+  const long long TC = (long long)NGR * a.ws_pref[a.S + 1 + a.S];
+  const long long cbase = (long long)NGR * a.ws_pref[a.S + 1 + s] + (long long)(g / HG) * (n + kSegCost) + kSegCost;
+  const long long w0 = balanced_wave_of(cbase, TC, W_eff);  // first and last worker of the segment
+  const long long w1 = balanced_wave_of(cbase + n - 1, TC, W_eff);
   const int hsub = g % HG;
   if (w0 == w1) return;
   const int k = (int)(w1 - w0 + 1);
@@ -1097,9 +1150,10 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_wide_kernel(D
   const long long T = (long long)NGR * a.ws_pref[a.S];
   const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
   const int n = (L + kChunk - 1) / kChunk;
-  const long long base = (long long)NGR * a.ws_pref[s] + (long long)(g / HG) * n;
-  const long long w0 = balanced_wave_of(base, T, W_eff);  // first and last worker of the segment
-  const long long w1 = balanced_wave_of(base + n - 1, T, W_eff);
+  const long long TC = (long long)NGR * a.ws_pref[a.S + 1 + a.S];
+  const long long cbase = (long long)NGR * a.ws_pref[a.S + 1 + s] + (long long)(g / HG) * (n + kSegCost) + kSegCost;
+  const long long w0 = balanced_wave_of(cbase, TC, W_eff);  // first and last worker of the segment
+  const long long w1 = balanced_wave_of(cbase + n - 1, TC, W_eff);
   const int hsub = g % HG;
   if (w0 == w1) return;  // uniform over the workgroup
   const int k = (int)(w1 - w0 + 1);
@@ -1170,7 +1224,7 @@ hipError_t launch_stage1(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.grid);
   const dim3 block(kThreads);
   if (p.schedule == kBalanced) {
-    const size_t lds = (size_t)(2 * p.S + 1) * sizeof(int);
+    const size_t lds = (size_t)(3 * p.S + 2) * sizeof(int);
     hipLaunchKernelGGL((decode_balanced_kernel<Core>), grid, block, lds, stream, p);
   } else {
     hipLaunchKernelGGL((decode_partitioned_kernel<Core>), grid, block, 0, stream, p);

@@ -29,7 +29,7 @@ struct Plan {
   int grid = 0;
   size_t acc_bytes = 0;  // workspace region of partial accumulators
   size_t ml_bytes = 0;   // workspace region of partial (max, sum) pairs
-  size_t pref_bytes = 0; // workspace region of per-sequence chunk prefix sums (balanced)
+  size_t pref_bytes = 0; // workspace region of per-sequence chunk and cost prefix sums (balanced)
   size_t total() const { return acc_bytes + ml_bytes + pref_bytes; }
 };
 
@@ -85,7 +85,7 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
     const size_t rows = (size_t)waves * 2 * group;  // two partial slots per wave, a row per query head
     plan->acc_bytes = round_up(rows * head_dim * sizeof(float), 256);
     plan->ml_bytes = round_up(rows * 2 * sizeof(float), 256);
-    plan->pref_bytes = round_up(((size_t)num_seqs + 1) * sizeof(int32_t), 256);
+    plan->pref_bytes = round_up(2 * ((size_t)num_seqs + 1) * sizeof(int32_t), 256);
     return PKV_OK;
   }
 

@@ -63,7 +63,7 @@ struct DecodeParams {
   float* out;             // [S, Hq, D]
   float* ws_acc;          // partial accumulators (rows of D)
   float2* ws_ml;          // partial (max, sum) pairs, one per accumulator row
-  int32_t* ws_pref;       // balanced: [S + 1] chunk prefix sums
+  int32_t* ws_pref;       // balanced: [S + 1] chunk prefix sums, then [S + 1] cost prefix sums
   const void* q;          // [S, Hq, D]
   const void* k;          // [NB, B, Hkv, D]
   const void* v;          // [NB, B, Hkv, D]
