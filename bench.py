@@ -14,8 +14,10 @@ step appends the token at position L and attends over L + 1 tokens.
 prints one JSON line: KV GB/s of the whole step (logical K+V bytes read by
 the attention, sum(L+1) * 2 * kv_heads * head_dim * 2 B, per step time), the
 roofline of the dominant kernel (stage 1, its duration from HIP events
-recorded around it on the launch stream inside the timed region, created
-without the system-scope fence that default events add; its HBM
+recorded around it on the launch stream in every fifth step of the timed
+region, created without the system-scope fence that default events add;
+each event still leaves a bubble of a few microseconds, so the other steps
+run unbracketed; its HBM
 traffic from the committed rocprofv3 counter summary when that was taken on
 the same kernel source), and the fp64 CPU oracle timed on the host's cores
 over the same workload.
@@ -72,6 +74,9 @@ def parse():
                     help="also time this many single decode launches after a 1 GiB cache flush each")
     ap.add_argument("--cow-pairs", type=int, default=2048,
                     help="block pairs in the copy-on-write block copy timed after the step (0 = skip)")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="bracket the stage-1 launch with HIP events in every n-th timed step (each event "
+                         "leaves a bubble of a few microseconds on the stream)")
     ap.add_argument("--swap-blocks", type=int, default=512,
                     help="blocks swapped out to pinned host memory and back after the step (0 = skip)")
     ap.add_argument("--no-prefill", action="store_true",
@@ -334,16 +339,23 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps; two events per step bracket the stage-1 launch.
-    ev = HipEvents(2 * args.steps, stream_ptr)
+    # Timed region: K whole steps; in every n-th step two events bracket the
+    # stage-1 launch (an event record leaves a bubble of a few microseconds
+    # between kernels, so the other steps run back to back).
+    every = max(1, args.event_every)
+    sampled = list(range(0, args.steps, every))
+    ev = HipEvents(2 * len(sampled), stream_ptr)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev, i)
+        if i % every == 0:
+            step(ev, i // every)
+        else:
+            step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    part_ms = float(np.mean([ev.ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+    part_ms = float(np.mean([ev.ms(2 * j, 2 * j + 1) for j in range(len(sampled))]))
     ev.close()
 
     # After the timed region: the other two launches, each bracketed alone.
@@ -372,7 +384,8 @@ def main():
         "pct_of_hbm_peak_step": 100.0 * value / HBM_PEAK_GBS,
         "seq_tokens_per_s": tokens / (ms_step / 1e3),
         "decode_tokens_per_s": w.num_seqs / (ms_step / 1e3),
-        "partition_kernel_ms": part_ms, "reduce_kernel_ms_untimed": red_ms,
+        "partition_kernel_ms": part_ms, "partition_kernel_samples": len(sampled),
+        "reduce_kernel_ms_untimed": red_ms,
         "append_at_kernel_ms_untimed": app_ms,
         "schedule": "balanced" if balanced else "partitioned",
         "partition_size": P, "num_partitions": NP,
