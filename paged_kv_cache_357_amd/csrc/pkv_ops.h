@@ -8,6 +8,9 @@
 
 namespace pkv {
 
+// Prompt pass: 16-column query tiles per wave.
+constexpr int kPrefillTilesPerWave = 2;
+
 // Arguments of the prompt (prefill) attention kernel.
 struct PrefillParams {
   float* out;               // [total_q, Hq, D]

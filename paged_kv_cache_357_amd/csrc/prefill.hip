@@ -60,20 +60,25 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
 // softmax reference.
 constexpr float kLazy = 8.0f;
 
-// Three waves per SIMD: with that register budget the accumulators stay in
+// Query tiles per wave: each K operand read and each assembled V operand
+// feeds NT products, and the NT softmax chains interleave.
+constexpr int kTilesPerWave = kPrefillTilesPerWave;
+
+// Two waves per SIMD: with that register budget the accumulators stay in
 // VGPRs (left to itself the compiler parks them in AGPRs and pays a copy
-// each way around every rescale, about 15% of the pass).
+// each way around every rescale).
 template <int D, int B, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(PrefillParams a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillParams a) {
   constexpr int ROW = D * 2;            // bytes of one token row of one kv head
   constexpr int LPR = ROW / 16;         // 16-byte pieces per row
   constexpr int KSTEPS = D / 32;
   constexpr int CW = D / 16;            // bf16 per lane of a V row = output tiles
-  constexpr int QT = 16 / G;            // tokens per wave tile
+  constexpr int QT = 16 / G;            // tokens per 16-column tile
+  constexpr int NT = kTilesPerWave;
+  constexpr int WT = NT * QT;           // tokens per wave
   constexpr int STEP = 2 * kChunk;      // keys per step: two 16-key halves
   constexpr int TILE = STEP * ROW;      // bytes of one step of K (or V)
   static_assert(kThreads >= kChunk * LPR, "one load per thread covers a half");
-  using VRow = typename std::conditional<CW == 8, u32x4, u32x2>::type;
   __shared__ __attribute__((aligned(16))) char s_k[2][TILE];
   __shared__ __attribute__((aligned(16))) char s_v[2][TILE];
 
@@ -87,44 +92,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
-  const int wg_t0 = wgt * kWavesPerWG * QT;
+  const int wg_t0 = wgt * kWavesPerWG * WT;
   if (wg_t0 >= n) return;  // uniform over the workgroup
   const int L = a.lens[s];
   const int cl = lane & 15, gl = lane >> 4;
-  const int t0 = wg_t0 + wave * QT;
-  const int t = t0 + cl / G;               // this lane's column: token t, head h of the group
-  const int h = cl % G;
-  const bool col_ok = t < n;
-  float* orow = a.out + ((size_t)(r0 + t) * a.Hq + (size_t)g * G + h) * D;
+  const int t0 = wg_t0 + wave * WT;
+  const int h = cl % G;                    // this lane's column in tile k: token t0 + k QT + cl / G, head h
+  int tk[NT];
+  bool ok[NT];
+  float* orow[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    tk[k] = t0 + k * QT + cl / G;
+    ok[k] = tk[k] < n;
+    orow[k] = a.out + ((size_t)(r0 + tk[k]) * a.Hq + (size_t)g * G + h) * D;
+  }
   if (L < n || L > a.max_len) {            // lengths that cannot hold the chunk: NaN rows
-    if (col_ok)
-      for (int d = gl; d < D; d += 4) orow[d] = __builtin_nanf("");
+#pragma unroll
+    for (int k = 0; k < NT; ++k)
+      if (ok[k])
+        for (int d = gl; d < D; d += 4) orow[k][d] = __builtin_nanf("");
     return;
   }
-  const int p_col = col_ok ? L - n + t : -1;                         // last key this column sees
-  const int p_wave = t0 < n ? L - n + min(t0 + QT, n) - 1 : -1;      // last key of this wave
-  const int p_wg = L - n + min(wg_t0 + kWavesPerWG * QT, n) - 1;     // last key of the workgroup
+  int p_col[NT];                                                      // last key each column sees
+#pragma unroll
+  for (int k = 0; k < NT; ++k) p_col[k] = ok[k] ? L - n + tk[k] : -1;
+  const int p_wave = t0 < n ? L - n + min(t0 + WT, n) - 1 : -1;       // last key of this wave
+  const int p_wg = L - n + min(wg_t0 + kWavesPerWG * WT, n) - 1;      // last key of the workgroup
   const int n_steps = p_wg / STEP + 1;
   const int32_t* trow = a.tables + (size_t)s * a.MB;
   const uint32_t rs = (uint32_t)a.Hkv * ROW;
   const char* kbase = static_cast<const char*>(a.k) + (size_t)g * ROW;
   const char* vbase = static_cast<const char*>(a.v) + (size_t)g * ROW;
 
-  // q^T operand: column cl is query row r0 + t, head g * G + h.
-  bf16x8 q[KSTEPS];
-  {
-    const char* qsrc = static_cast<const char*>(a.q) + ((size_t)(r0 + t) * a.Hq + (size_t)g * G + h) * ROW;
+  // q^T operands: column cl of tile k is query row r0 + tk[k], head g * G + h.
+  bf16x8 q[NT][KSTEPS];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    const char* qsrc = static_cast<const char*>(a.q) + ((size_t)(r0 + tk[k]) * a.Hq + (size_t)g * G + h) * ROW;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
       uint4 v4 = make_uint4(0, 0, 0, 0);
-      if (col_ok) v4 = *reinterpret_cast<const uint4*>(qsrc + 16 * (gl + 4 * j));
-      q[j] = __builtin_bit_cast(bf16x8, make_u32x4(v4));
+      if (ok[k]) v4 = *reinterpret_cast<const uint4*>(qsrc + 16 * (gl + 4 * j));
+      q[k][j] = __builtin_bit_cast(bf16x8, make_u32x4(v4));
     }
   }
-  f32x4 acc[CW];
+  f32x4 acc[NT][CW];
+  float m_run[NT], l_run[NT];
 #pragma unroll
-  for (int dt = 0; dt < CW; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = kNegBig, l_run = 0.0f;
+  for (int k = 0; k < NT; ++k) {
+#pragma unroll
+    for (int dt = 0; dt < CW; ++dt) acc[k][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run[k] = kNegBig;
+    l_run[k] = 0.0f;
+  }
 
   // Step loads: for each 16-key half, thread tid moves 16 bytes (piece
   // tid % LPR of row tid / LPR) of K and of V.  Halves past the last needed
@@ -155,6 +176,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       vr[half] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0));
     }
   };
+  // V goes into LDS already in operand order: for output tile dt and lane
+  // (gl, cl) the eight bf16 of k slots 0..7 (keys 4 gl + 0..3, 16 + 4 gl +
+  // 0..3) at column d = CW cl + dt sit in 16 consecutive bytes, so each wave
+  // reads its V operand with one 16-byte read per tile and no shuffling.
+  // This thread holds d = 8 lc .. 8 lc + 7 of key row lr of each half.
+  int vt_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int d = 8 * lc + i;
+    const int vcl = d / CW, vdt = d % CW;
+    vt_off[i] = ((vdt * 64 + (lr / 4) * 16 + vcl) * 8 + (lr % 4)) * 2;  // + 8 bytes for the second half
+  }
   auto store = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
     if (!loader) return;
 #pragma unroll
@@ -163,37 +196,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       // K: piece lc of row r at (lc ^ (r mod LPR)), so the operand reads
       // (16 rows at one piece) fall in distinct banks.
       *reinterpret_cast<u32x4*>(s_k[buf] + r * ROW + ((lc ^ (r % LPR)) * 16)) = kr[half];
-      *reinterpret_cast<u32x4*>(s_v[buf] + r * ROW + lc * 16) = vr[half];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t wd = vr[half][i / 2];
+        const unsigned short v16 = (unsigned short)((i % 2 == 0) ? (wd & 0xffffu) : (wd >> 16));
+        *reinterpret_cast<unsigned short*>(s_v[buf] + vt_off[i] + half * 8) = v16;
+      }
     }
   };
 
-  // One 32-key step for this wave's 16 columns.  Lane (gl, cl) ends the
-  // score products holding keys 4 gl + r (first half) and 16 + 4 gl + r
-  // (second half), r = 0..3, of column cl.  The V product contracts over 32
-  // keys with one 16x16x32 product per output tile; its k index order is
-  // the same for both operands (k slot 8 gl + i is key 4 gl + i for i < 4,
-  // 16 + 4 gl + i - 4 after), so the lane's eight weights are its B operand
-  // as they stand.
+  // One 32-key step for this wave's NT tiles of 16 columns.  Lane (gl, cl)
+  // ends the score products holding keys 4 gl + r (first half) and
+  // 16 + 4 gl + r (second half), r = 0..3, of its column in each tile.  The
+  // V product contracts over 32 keys with one 16x16x32 product per output
+  // tile; its k index order is the same for both operands (k slot 8 gl + i
+  // is key 4 gl + i for i < 4, 16 + 4 gl + i - 4 after), so the lane's eight
+  // weights are its B operand as they stand.
   auto compute = [&](int c, int buf) {
     const int cs = c * STEP;
-    const int lim = p_col - cs;
-    f32x4 sc[2];
+    f32x4 sc[NT][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      sc[half] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < NT; ++k) sc[k][half] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const int r = half * kChunk + cl;
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) {
         const int pc = (gl + 4 * j) ^ (r % LPR);
-        const u32x4 k = *reinterpret_cast<const u32x4*>(s_k[buf] + r * ROW + pc * 16);
-        sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), q[j], sc[half], 0, 0, 0);
-      }
-    }
-    VRow vrow[8];
+        const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k[buf] + r * ROW + pc * 16));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (i < 4 ? 0 : kChunk) + 4 * gl + (i & 3);
-      vrow[i] = *reinterpret_cast<const VRow*>(s_v[buf] + r * ROW + cl * (2 * CW));
+        for (int k = 0; k < NT; ++k) sc[k][half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[k][j], sc[k][half], 0, 0, 0);
+      }
     }
 
     // Online softmax with a lazily moved reference: the running reference
@@ -202,102 +235,97 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // accumulator is rescaled rarely.  Any reference gives the same
     // softmax; only rounding depends on it, and it depends on the data
     // alone, so results stay deterministic.
-    float x[8];
-    float mx = kNegBig;
+    bf16x8 phi[NT], plo[NT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = (i < 4 ? 0 : kChunk) + 4 * gl + (i & 3);
-      x[i] = (key <= lim) ? sc[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool move = mx > m_run + kLazy;
-    if (__any(move)) {
-      const float m_new = move ? mx : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < CW; ++dt) acc[dt] *= alpha;
-    }
-    float pw[8];
-    float ps = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pw[i] = fast_exp2(x[i] - m_run);
-      ps += pw[i];
-    }
-    l_run += ps;
-
-    // P^T operand, high (truncated) and low (rounded rest) bf16 parts.
-    uint32_t hb[8];
-    float res[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      hb[i] = __float_as_uint(pw[i]) & 0xffff0000u;
-      res[i] = pw[i] - __uint_as_float(hb[i]);
-    }
-    const bf16x8 phi = __builtin_bit_cast(
-        bf16x8, u32x4{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3], (hb[4] >> 16) | hb[5], (hb[6] >> 16) | hb[7]});
-    const bf16x8 plo = __builtin_bit_cast(
-        bf16x8, u32x4{pack_bf16_rne(res[0], res[1]), pack_bf16_rne(res[2], res[3]), pack_bf16_rne(res[4], res[5]),
-                      pack_bf16_rne(res[6], res[7])});
-#pragma unroll
-    for (int dt = 0; dt < CW; ++dt) {
-      // element dt of the eight key rows, in k slot order
-      uint32_t e[8];
+    for (int k = 0; k < NT; ++k) {
+      const int lim = p_col[k] - cs;
+      float x[8];
+      float mx = kNegBig;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t wd = vrow[i][dt / 2];
-        e[i] = (dt % 2 == 0) ? (wd & 0xffffu) : (wd >> 16);
+        const int key = (i < 4 ? 0 : kChunk) + 4 * gl + (i & 3);
+        x[i] = (key <= lim) ? sc[k][i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[i]);
       }
-      const bf16x8 vt = __builtin_bit_cast(
-          bf16x8, u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)});
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo, acc[dt], 0, 0, 0);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool move = mx > m_run[k] + kLazy;
+      if (__any(move)) {
+        const float m_new = move ? mx : m_run[k];
+        const float alpha = fast_exp2(m_run[k] - m_new);
+        m_run[k] = m_new;
+        l_run[k] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < CW; ++dt) acc[k][dt] *= alpha;
+      }
+      float pw[8];
+      float ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pw[i] = fast_exp2(x[i] - m_run[k]);
+        ps += pw[i];
+      }
+      l_run[k] += ps;
+      // P^T operand, high (truncated) and low (rounded rest) bf16 parts.
+      uint32_t hb[8];
+      float res[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hb[i] = __float_as_uint(pw[i]) & 0xffff0000u;
+        res[i] = pw[i] - __uint_as_float(hb[i]);
+      }
+      phi[k] = __builtin_bit_cast(
+          bf16x8, u32x4{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3], (hb[4] >> 16) | hb[5], (hb[6] >> 16) | hb[7]});
+      plo[k] = __builtin_bit_cast(
+          bf16x8, u32x4{pack_bf16_rne(res[0], res[1]), pack_bf16_rne(res[2], res[3]), pack_bf16_rne(res[4], res[5]),
+                        pack_bf16_rne(res[6], res[7])});
+    }
+#pragma unroll
+    for (int dt = 0; dt < CW; ++dt) {
+      const bf16x8 vt =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_v[buf] + (dt * 64 + gl * 16 + cl) * 16));
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        acc[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[k], acc[k][dt], 0, 0, 0);
+        acc[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[k], acc[k][dt], 0, 0, 0);
+      }
     }
   };
 
-  // Step loop: the next PD steps are loaded ahead into registers; step c is
-  // computed from one LDS buffer while step c+1 goes into the other, one
-  // barrier per step.  Slot k of the register ring holds steps k, k+PD, ..
-  // (Deeper prefetch measured no faster: the pass is bound by the wave's
-  // own instruction chain, not by load latency.)
-  constexpr int PD = 1;
-  u32x4 kr[PD][2], vr[PD][2];
-#pragma unroll
-  for (int k = 0; k < PD; ++k) load(k, kr[k], vr[k]);
-  store(0, kr[0], vr[0]);
+  // Step loop: the next step is loaded into registers while step c is
+  // computed from one LDS buffer, then stored into the other; one barrier
+  // per step.  (Deeper prefetch measured no faster: the pass is bound by the
+  // wave's own instruction chain, not by load latency.)
+  u32x4 kr[2], vr[2];
+  load(0, kr, vr);
+  store(0, kr, vr);
   __syncthreads();
-  for (int c0 = 0; c0 < n_steps; c0 += PD) {
-#pragma unroll
-    for (int k = 0; k < PD; ++k) {
-      const int c = c0 + k;
-      if (c >= n_steps) break;  // uniform over the workgroup
-      load(c + PD, kr[k], vr[k]);  // slot k is free: step c went to LDS one step ago
-      if (c * STEP <= p_wave) compute(c, c & 1);
-      if (c + 1 < n_steps) store((c + 1) & 1, kr[(k + 1) % PD], vr[(k + 1) % PD]);
-      __syncthreads();
-    }
+  for (int c = 0; c < n_steps; ++c) {
+    if (c + 1 < n_steps) load(c + 1, kr, vr);
+    if (c * STEP <= p_wave) compute(c, c & 1);
+    if (c + 1 < n_steps) store((c + 1) & 1, kr, vr);
+    __syncthreads();
   }
   bad = __syncthreads_or(bad);
 
   // Lane (gl, cl) holds output columns CW * (4 gl + r) + dt of its row; the
   // four lane groups share the running reference, their sums add.
-  float lt = l_run + __shfl_xor(l_run, 16);
-  lt += __shfl_xor(lt, 32);
-  if (!col_ok) return;
   const int col0 = 4 * CW * gl;
   const float nan = __builtin_nanf("");
-  float4* dst = reinterpret_cast<float4*>(orow + col0);
 #pragma unroll
-  for (int e = 0; e < 4 * CW; e += 4) {
-    float v4[4];
+  for (int k = 0; k < NT; ++k) {
+    float lt = l_run[k] + __shfl_xor(l_run[k], 16);
+    lt += __shfl_xor(lt, 32);
+    if (!ok[k]) continue;
+    float4* dst = reinterpret_cast<float4*>(orow[k] + col0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v4[i] = acc[(e + i) % CW][(e + i) / CW];
-    dst[e / 4] = bad ? make_float4(nan, nan, nan, nan)
-                     : make_float4(v4[0] / lt, v4[1] / lt, v4[2] / lt, v4[3] / lt);
+    for (int e = 0; e < 4 * CW; e += 4) {
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = acc[k][(e + i) % CW][(e + i) / CW];
+      dst[e / 4] = bad ? make_float4(nan, nan, nan, nan)
+                       : make_float4(v4[0] / lt, v4[1] / lt, v4[2] / lt, v4[3] / lt);
+    }
   }
 }
 
