@@ -1042,29 +1042,29 @@ void decode_balanced_kernel(DecodeParams a) {
   }
 }
 
-// Stage 2 of the balanced schedule: one wave per query-head row (s, h), h in
-// the group of kv head g, four rows per workgroup.  An invalid length gives a
-// NaN row and L = 0 zeros; a segment that one wave finished was written by
-// stage 1; otherwise the pieces of waves w0 .. w1 (slot 1 of w0, slot 0 of
-// the later ones) are merged in wave order: exp2(m_w - M) * (acc_w, l_w)
-// summed, M the largest m_w.  Lane j owns columns j*CPL .. j*CPL + CPL - 1.
-template <int D>
+// Stage 2 of the balanced schedule: one wave per segment (s, g), taking the
+// G query-head rows h of kv head g in turn, four segments per workgroup.  An
+// invalid length gives NaN rows and L = 0 zeros; a segment that one wave
+// finished was written by stage 1; otherwise the pieces of waves w0 .. w1
+// (slot 1 of w0, slot 0 of the later ones) are merged in wave order:
+// exp2(m_w - M) * (acc_w, l_w) summed, M the largest m_w.  Lane j owns
+// columns j*CPL .. j*CPL + CPL - 1.
+template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(DecodeParams a) {
   constexpr int CPL = D / 64;  // columns per lane (1 or 2)
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWavesPerWG + uniform(threadIdx.x >> 6);  // s * Hq + query head
-  if (row >= a.S * a.Hq) return;
-  const int s = row / a.Hq;
-  const int hq = row - s * a.Hq;
-  const int G = a.Hq / a.Hkv;
-  const int g = hq / G;
-  const int h = hq - g * G;
+  const int seg = blockIdx.x * kWavesPerWG + uniform(threadIdx.x >> 6);  // s * Hkv + kv head
+  if (seg >= a.S * a.Hkv) return;
+  const int s = seg / a.Hkv;
+  const int g = seg - s * a.Hkv;
   const int L = a.lens[s];
-  float* o = a.out + (size_t)row * D + lane * CPL;
+  float* o0 = a.out + ((size_t)s * a.Hq + (size_t)g * G) * D + lane * CPL;  // row h at o0 + h * D
   if (L < 0 || L > a.max_len || L == 0) {
     const float fill = L == 0 ? 0.0f : __builtin_nanf("");
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) o[j] = fill;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) o0[(size_t)h * D + j] = fill;
     return;
   }
   const int HG = a.head_group;
@@ -1079,43 +1079,56 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(Decode
   const int hsub = g % HG;
   if (w0 == w1) return;
   const int k = (int)(w1 - w0 + 1);
-  auto piece_row = [&](int p) -> size_t {
+  auto piece_row = [&](int p) -> size_t {  // row of head 0 of the group; head h is + h
     const size_t wave_id = HG == 1 ? (size_t)(w0 + p) : (size_t)(w0 + p) * kWavesPerWG + hsub;
-    return (wave_id * 2 + (p == 0 ? 1 : 0)) * G + h;
+    return (wave_id * 2 + (p == 0 ? 1 : 0)) * G;
   };
 
-  float M = kNegBig;
-  for (int p = lane; p < k; p += 64) M = fmaxf(M, a.ws_ml[piece_row(p)].x);
+  float M[G];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  for (int h = 0; h < G; ++h) M[h] = kNegBig;
+  for (int p = lane; p < k; p += 64) {
+    const size_t r = piece_row(p);
+#pragma unroll
+    for (int h = 0; h < G; ++h) M[h] = fmaxf(M[h], a.ws_ml[r + h].x);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M[h] = fmaxf(M[h], __shfl_xor(M[h], off));
 
-  float num[CPL], den = 0.0f;
+  float num[G][CPL], den[G];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) num[j] = 0.0f;
-  // eight pieces per step, so eight loads are in flight at once
-  for (int p0 = 0; p0 < k; p0 += 8) {
+  for (int h = 0; h < G; ++h) {
+    den[h] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = p0 + i;
-      if (p < k) {
-        const size_t r = piece_row(p);
-        const float2 t = a.ws_ml[r];
-        const float f = fast_exp2(t.x - M);
-        den = fmaf(t.y, f, den);
-        if constexpr (CPL == 2) {
-          const float2 x = *reinterpret_cast<const float2*>(a.ws_acc + r * D + lane * CPL);
-          num[0] = fmaf(x.x, f, num[0]);
-          num[1] = fmaf(x.y, f, num[1]);
-        } else {
-          num[0] = fmaf(a.ws_acc[r * D + lane], f, num[0]);
-        }
+    for (int j = 0; j < CPL; ++j) num[h][j] = 0.0f;
+  }
+  // pieces in wave order; the G rows of a piece are loaded together
+  for (int p = 0; p < k; ++p) {
+    const size_t r = piece_row(p);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float2 t = a.ws_ml[r + h];
+      const float f = fast_exp2(t.x - M[h]);
+      den[h] = fmaf(t.y, f, den[h]);
+      if constexpr (CPL == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(a.ws_acc + (r + h) * D + lane * CPL);
+        num[h][0] = fmaf(x.x, f, num[h][0]);
+        num[h][1] = fmaf(x.y, f, num[h][1]);
+      } else {
+        num[h][0] = fmaf(a.ws_acc[(r + h) * D + lane], f, num[h][0]);
       }
     }
   }
-  if constexpr (CPL == 2) {
-    *reinterpret_cast<float2*>(o) = make_float2(num[0] / den, num[1] / den);
-  } else {
-    o[0] = num[0] / den;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float* o = o0 + (size_t)h * D;
+    if constexpr (CPL == 2) {
+      *reinterpret_cast<float2*>(o) = make_float2(num[h][0] / den[h], num[h][1] / den[h]);
+    } else {
+      o[0] = num[h][0] / den[h];
+    }
   }
 }
 
@@ -1271,9 +1284,21 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_d
                     : launch_d<0>(p, head_dim, block_size, group, stream);
 }
 
+template <int D>
+hipError_t launch_narrow_merge(const DecodeParams& p, int group, dim3 grid, hipStream_t stream) {
+  switch (group) {
+    case 1: hipLaunchKernelGGL((decode_reduce_balanced_kernel<D, 1>), grid, dim3(kThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_reduce_balanced_kernel<D, 2>), grid, dim3(kThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_reduce_balanced_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_reduce_balanced_kernel<D, 8>), grid, dim3(kThreads), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((decode_reduce_balanced_kernel<D, 16>), grid, dim3(kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, int group, hipStream_t stream) {
   if (p.S == 0) return hipSuccess;
-  (void)group;
   if (p.schedule == kBalanced) {
     // Segments are cut into about W / (S * Hkv) pieces when the lengths are
     // alike; many pieces per segment get four waves per row.
@@ -1286,12 +1311,10 @@ hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, int group, 
         default: return hipErrorInvalidValue;
       }
     } else {
-      const dim3 grid((unsigned)(((long long)p.S * p.Hq + kWavesPerWG - 1) / kWavesPerWG));
-      switch (head_dim) {
-        case 64: hipLaunchKernelGGL((decode_reduce_balanced_kernel<64>), grid, dim3(kThreads), 0, stream, p); break;
-        case 128: hipLaunchKernelGGL((decode_reduce_balanced_kernel<128>), grid, dim3(kThreads), 0, stream, p); break;
-        default: return hipErrorInvalidValue;
-      }
+      const dim3 grid((unsigned)(((long long)p.S * p.Hkv + kWavesPerWG - 1) / kWavesPerWG));
+      if (head_dim == 64) return launch_narrow_merge<64>(p, group, grid, stream);
+      if (head_dim == 128) return launch_narrow_merge<128>(p, group, grid, stream);
+      return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
