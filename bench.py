@@ -1,9 +1,11 @@
 """Benchmark: one decode step of paged attention on one MI355X.
 
 A step is the whole path over one batch: slot mapping for every sequence's
-new token and the K/V append into its block (one launch), the fused score / online-softmax /
+new token and the K/V append into its block, the fused score / online-softmax /
 V pass over every sequence's physical blocks (stage 1), and the merge of the
-pieces of split segments (stage 2).  The
+pieces of split segments (stage 2).  By default the append is a launch of its
+own before stage 1; --fused-append runs paged_attn_decode_append instead,
+where stage 1 writes the new rows itself.  The
 workload is the Llama-7B-shaped decode batch (64 sequences, context lengths
 uniform in [128, 2048], 32 query / 32 kv heads, head_dim 128, bf16 K/V in
 16-token blocks dealt from a shuffled pool 1.25x the blocks in use).  Each
@@ -68,6 +70,8 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--deal", default="shuffled", choices=["shuffled", "identity"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-append", action="store_true",
+                    help="fuse the append into stage 1 (paged_attn_decode_append) instead of its own launch")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = all)")
     ap.add_argument("--probes", action="store_true", help="also time plain HBM read / copy probes")
     ap.add_argument("--flush-reps", type=int, default=0,
@@ -328,14 +332,21 @@ def main():
     lens = torch.from_numpy(lens_step).to(dev)
     max_len = int(lens_step.max())
     slots = torch.empty(w.num_seqs, dtype=torch.int32, device=dev)
-    call = pk.DecodeCall(q, kc, vc, tables, lens, w.scale, max_len, args.partition_size)
+    two_launch = not args.fused_append
+    if two_launch:
+        # slot mapping + K/V append in a launch of its own, then the decode of L + 1
+        call = pk.DecodeCall(q, kc, vc, tables, lens, w.scale, max_len, args.partition_size)
+    else:
+        # the append fused into stage 1: the wave that streams position L writes it first
+        call = pk.DecodeAppendCall(q, kc, vc, kn, vn, tables, pos, w.scale, max_len, args.partition_size)
     P, NP = call.plan
     balanced = P == 0  # balanced schedule: NP is the number of worker waves
 
     stream_ptr = torch.cuda.current_stream(dev).cuda_stream  # the stream every entry point launches on
 
     def step(ev=None, i=0):
-        pk.append_at(kc, vc, kn, vn, tables, pos, slots)  # slot mapping + K/V append, one launch
+        if two_launch:
+            pk.append_at(kc, vc, kn, vn, tables, pos, slots)  # slot mapping + K/V append, one launch
         if ev is not None:
             ev.record(2 * i)
         call.partitions()
@@ -366,7 +377,9 @@ def main():
     part_ms = float(np.mean([ev.ms(2 * j, 2 * j + 1) for j in range(len(sampled))]))
     ev.close()
 
-    # After the timed region: the other two launches, each bracketed alone.
+    # After the timed region: the other launches, each bracketed alone (the
+    # separate append only exists on the two-launch path; it is timed there
+    # and, for comparison, also here).
     ev = HipEvents(4 * 10, stream_ptr)
     for i in range(10):
         ev.record(4 * i)
@@ -395,6 +408,7 @@ def main():
         "partition_kernel_ms": part_ms, "partition_kernel_samples": len(sampled),
         "reduce_kernel_ms_untimed": red_ms,
         "append_at_kernel_ms_untimed": app_ms,
+        "append": "separate launch (append_at)" if two_launch else "fused into stage 1",
         "schedule": "balanced" if balanced else "partitioned",
         "partition_size": P, "num_partitions": NP,
         "kernel_sha": kernel_sha(),

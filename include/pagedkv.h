@@ -212,6 +212,66 @@ PKV_API int paged_attn_decode_reduce(float* out, const void* q, const void* k_ca
                              size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode_append — a decode step that appends and attends in one
+ * pass: the slot write of each sequence's new token ("PagedAttention and vLLM
+ * Architecture", Why Internal Fragmentation is Bounded: a sequence holding L
+ * tokens puts its next one at position L, into the block the engine added to
+ * its table when L reached a block boundary; the slot is T[L / B] * B + L % B,
+ * "PagedAttention Paper Breakdown", section 2) fused with paged_attn_decode
+ * over the L + 1 tokens that then make up the context.  For every sequence s
+ * with L = context_lens[s] (the length before the append):
+ *
+ *   K_L, V_L := k_new[s], v_new[s]   (bit copy into slot T[s][L / B] * B + L % B)
+ *   out[s,h,:] = paged_attn_decode over positions 0 .. L
+ *
+ * The result equals paged_kv_append_at(positions = context_lens) followed by
+ * paged_attn_decode with context_lens + 1, bitwise, in one launch fewer: the
+ * wave that streams the chunk holding position L writes the new row first.
+ *
+ *   k_cache, v_cache [num_blocks, block_size, kv_heads, head_dim] dtype, in/out:
+ *                the new rows are written, nothing else.
+ *   k_new, v_new [num_seqs, kv_heads, head_dim] dtype, read.
+ *   context_lens [num_seqs] int32, lengths before the append.  A sequence with
+ *                L < 0 or L + 1 > max_context_len gets NaN rows and no write.
+ *                A table entry outside [0, num_blocks) among its first
+ *                ceil((L + 1) / B) gives NaN rows; if it is the entry of
+ *                block L / B, nothing is written either.
+ *   max_context_len  host-side bound of the attended length L + 1; sizes the
+ *                grid and the workspace (paged_attn_decode_workspace_size with
+ *                the same value).  Must be <= max_blocks_per_seq * block_size.
+ *   Everything else as paged_attn_decode.  The new slots must be distinct
+ *   and must not lie in a block another sequence shares (copy-on-write first).
+ *
+ * Errors: those of paged_attn_decode; PKV_ERR_NULL also for a missing k_new
+ * or v_new.  The _partitions / _reduce pair splits the call into its two
+ * stages like paged_attn_decode_partitions / _reduce (the append happens in
+ * the first).
+ */
+PKV_API int paged_attn_decode_append(float* out, const void* q, void* k_cache, void* v_cache,
+                                     const void* k_new, const void* v_new, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                                     int32_t kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                     int32_t dtype, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+PKV_API int paged_attn_decode_append_partitions(float* out, const void* q, void* k_cache, void* v_cache,
+                                                const void* k_new, const void* v_new,
+                                                const int32_t* block_tables, const int32_t* context_lens,
+                                                int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
+                                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                                int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                                int32_t dtype, int32_t partition_size, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+PKV_API int paged_attn_decode_append_reduce(float* out, const void* q, void* k_cache, void* v_cache,
+                                            const void* k_new, const void* v_new, const int32_t* block_tables,
+                                            const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                                            int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                                            int32_t num_blocks, int32_t max_blocks_per_seq,
+                                            int32_t max_context_len, float scale, int32_t dtype,
+                                            int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/*
  * paged_attn_decode_plan — the schedule a call with these arguments uses
  * (partition_size 0 = the automatic choice).  Host only; writes
  * *resolved_partition_size and *num_partitions (either may be NULL):

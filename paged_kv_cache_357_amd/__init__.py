@@ -12,11 +12,13 @@ from ._lib import (  # noqa: F401
     DTYPE_F32,
     LIB_PATH,
     SIGNATURES,
+    DecodeAppendCall,
     DecodeCall,
     PagedKVError,
     append,
     append_at,
     decode,
+    decode_append,
     load_library,
     plan,
     prefill,

@@ -25,6 +25,7 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 # name -> (restype, argtypes); must match include/pagedkv.h
 _DECODE_ARGS = [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                 _c_f, _c_i32, _c_i32, _vp, _c_sz, _vp]
+_DECODE_APPEND_ARGS = [_vp] * 8 + [_c_i32] * 8 + [_c_f, _c_i32, _c_i32, _vp, _c_sz, _vp]
 SIGNATURES = {
     "paged_kv_slot_mapping": (_c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "paged_kv_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
@@ -33,6 +34,9 @@ SIGNATURES = {
     "paged_attn_decode": (_c_int, _DECODE_ARGS),
     "paged_attn_decode_partitions": (_c_int, _DECODE_ARGS),
     "paged_attn_decode_reduce": (_c_int, _DECODE_ARGS),
+    "paged_attn_decode_append": (_c_int, _DECODE_APPEND_ARGS),
+    "paged_attn_decode_append_partitions": (_c_int, _DECODE_APPEND_ARGS),
+    "paged_attn_decode_append_reduce": (_c_int, _DECODE_APPEND_ARGS),
     "paged_attn_decode_plan": (_c_int, [_c_i32] * 8 + [_i32p, _i32p]),
     "paged_attn_decode_workspace_size": (_c_sz, [_c_i32] * 8),
     "paged_status_str": (ctypes.c_char_p, [_c_int]),
@@ -443,6 +447,43 @@ class DecodeCall:
 
     def reduce(self):
         return self._call("paged_attn_decode_reduce")
+
+
+class DecodeAppendCall(DecodeCall):
+    """A prepared fused step: each sequence's new K/V row is written at
+    position context_lens[s] and the decode attends over context_lens[s] + 1
+    tokens, in the launches of one decode.  ``max_context_len`` bounds the
+    attended length (L + 1)."""
+
+    def __init__(self, q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, scale, max_context_len,
+                 partition_size=0, out=None, workspace=None):
+        super().__init__(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size,
+                         out, workspace)
+        Hkv, D = k_cache.shape[2], k_cache.shape[3]
+        S = q.shape[0]
+        _require(k_new.shape == (S, Hkv, D) and v_new.shape == (S, Hkv, D), "k_new / v_new must be [S, Hkv, D]")
+        _require(k_new.dtype == v_new.dtype == k_cache.dtype, "k_new / v_new must have the cache dtype")
+        _dev(q, k_new, v_new)
+        self._keep = self._keep + (k_new, v_new)
+        a = self.args
+        self.args = a[:4] + (_ptr(k_new), _ptr(v_new)) + a[4:]
+
+    def run(self):
+        return self._call("paged_attn_decode_append")
+
+    def partitions(self):
+        return self._call("paged_attn_decode_append_partitions")
+
+    def reduce(self):
+        return self._call("paged_attn_decode_append_reduce")
+
+
+def decode_append(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, scale, max_context_len,
+                  partition_size=0, out=None, workspace=None) -> torch.Tensor:
+    """Append each sequence's new token at position context_lens[s] and decode
+    over the context_lens[s] + 1 tokens; returns out [S, Hq, D] fp32."""
+    return DecodeAppendCall(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, scale, max_context_len,
+                            partition_size, out, workspace).run()
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size=0,

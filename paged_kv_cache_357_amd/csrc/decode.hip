@@ -74,7 +74,7 @@ namespace {
 
 constexpr float kNegBig = -1.0e30f;
 // Balanced schedule: the cost, in chunks, charged for starting a segment
-// (query rows, block-table window, piece epilogue) when the shares are cut.
+// (query rows, table entries, piece epilogue) when the shares are cut.
 // Measured: 2 evens out shares that start many short segments (lognormal
 // GQA batch +3%), and changes nothing measurable elsewhere.
 constexpr int kSegCost = 2;
@@ -94,6 +94,62 @@ constexpr int kStreamPolicy = PKV_NT_LOADS ? 2 : 0;
 constexpr int kBufferConfig = 0x00020000;
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Tokens sequence s attends to, or -1 for a length the launch cannot cover
+// (its rows become NaN).  With the fused append the stored length is the one
+// before the append: position L receives the new token and L + 1 tokens are
+// attended, so L + 1 must not exceed max_len.
+__device__ __forceinline__ int attended_len(const DecodeParams& a, int s) {
+  const int L = a.lens[s];
+  if (a.append) return (L >= 0 && L < a.max_len) ? L + 1 : -1;
+  return (L >= 0 && L <= a.max_len) ? L : -1;
+}
+
+// Fused append of one (sequence s, kv head g) row, as the partitioned
+// schedule does it: the new K and V rows go to position p, slot
+// T[p / B] * B + p % B of the pool ("PagedAttention Paper Breakdown", section
+// 2, Address Translation Formula; K and V share the slot).  Lanes 0 ..
+// ROW/16 - 1 carry 16 bytes each.  A block id outside [0, NB) writes nothing
+// (the table window check already turns the segment's rows into NaN).  The
+// unit that writes the row is the one that later streams that row's chunk,
+// and a wave's own memory operations on one address take effect in program
+// order, so its loads see the new row.  (The balanced schedule loads the
+// row ahead through its pipeline instead; see there.)
+struct NewRow {
+  uint4 k, v;
+  int blk;
+};
+
+template <int ROW>
+__device__ __forceinline__ NewRow load_new_row(const DecodeParams& a, int B, int s, int g, int p, int lane) {
+  NewRow r;
+  r.blk = a.tables[(size_t)s * a.MB + p / B];
+  r.k = make_uint4(0, 0, 0, 0);
+  r.v = r.k;
+  if (lane < ROW / 16) {
+    const size_t src = ((size_t)s * a.Hkv + g) * ROW + (size_t)lane * 16;
+    r.k = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
+    r.v = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src);
+  }
+  return r;
+}
+
+template <int ROW>
+__device__ __forceinline__ void store_new_row(const DecodeParams& a, int B, const NewRow& r, int g, int p, int lane) {
+  if (r.blk < 0 || r.blk >= a.NB || lane >= ROW / 16) return;
+  const size_t dst = (((size_t)r.blk * B + (size_t)(p % B)) * a.Hkv + g) * ROW + (size_t)lane * 16;
+  *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst) = r.k;
+  *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst) = r.v;
+}
+
+// What a balanced-schedule pipeline slot loads beside its chunk: the table
+// entry of the chunk issued into the slot next, and, with the fused append,
+// the new row of a segment that begins there (see the balanced kernel).
+struct AppendSlot {
+  int nid;         // table entry of the next chunk issued into this slot
+  NewRow row;      // fused append: the new K / V row and the table entry of its block
+  long long off;   // fused append: byte offset of the row inside its block, or -1: none
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -145,8 +201,9 @@ __device__ __forceinline__ int logical_workgroup(int b, int group, int n_wg) {
 }
 
 // Physical block ids of logical blocks base .. base+63 of a sequence, one
-// per lane (0 past its last block).  An id outside [0, NB) is replaced by 0 so
-// it is never dereferenced, and reported through *bad.
+// per lane (0 past its last block), for the partitioned schedule.  An id
+// outside [0, NB) is replaced by 0 so it is never dereferenced, and reported
+// through *bad.
 __device__ __forceinline__ int load_table_window(const int32_t* trow, int base, int n_blk, int lane, int NB,
                                                  bool* bad) {
   int b = 0;
@@ -193,6 +250,7 @@ struct ValuCore {
   struct Buf {
     u32x4 k[NI], v[NI];
     uint32_t q[G][4];
+    AppendSlot app;  // balanced schedule: table entry ahead, fused append
   };
 
   int grp, seg;
@@ -430,6 +488,7 @@ struct MfmaCore {
     u32x4 k[NK];
     VRow v[4];
     bf16x8 q[KSTEPS];
+    AppendSlot app;  // balanced schedule: table entry ahead, fused append
   };
 
   int gl, cl;
@@ -608,9 +667,9 @@ __global__ __launch_bounds__(kThreads) void decode_partitioned_kernel(DecodePara
   const int s = sp % a.S;
   const int part = sp / a.S;
 
-  const int L = a.lens[s];
+  const int L = attended_len(a, s);
   const int tok0 = part * a.P;
-  const bool bad_len = (L < 0) || (L > a.max_len);
+  const bool bad_len = L < 0;
   const bool direct = (L <= a.P);  // this sequence fits one partition: write out directly
   float* orow = a.out + ((size_t)s * a.Hq + (size_t)g * G) * D;
 
@@ -636,11 +695,17 @@ __global__ __launch_bounds__(kThreads) void decode_partitioned_kernel(DecodePara
 
   Core core;
   core.init(lane, rs, s_stage[wave]);
+  // Fused append: the unit holding the last position writes the new token
+  // before it loads any row.
+  const bool appends = a.append && L - 1 < tok_end;
+  NewRow nr;
+  if (appends) nr = load_new_row<ROW>(a, B, s, g, L - 1, lane);
   bool bad = false;
   int wbase = 0;
   int tbl = load_table_window(trow, 0, n_blk, lane, a.NB, &bad);
   core.load_q(a, s, g);
   core.reset();
+  if (appends) store_new_row<ROW>(a, B, nr, g, L - 1, lane);
 
   auto issue = [&](int c, typename Core::Buf& b) {
     const int cs = tok0 + c * kChunk;
@@ -705,8 +770,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_partitioned_kernel(Dec
   const int s = row / a.Hq;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int L = a.lens[s];
-  const bool bad_len = (L < 0) || (L > a.max_len);
+  const int L = attended_len(a, s);
+  const bool bad_len = L < 0;
   if (!bad_len && L <= a.P) return;  // written by stage 1 (or L = 0 zeros); uniform over the workgroup
   float* o = a.out + (size_t)row * D + lane * CPL;
   if (bad_len) {
@@ -807,7 +872,7 @@ __device__ __forceinline__ long long balanced_workers(long long T, int W) {
   return w < 1 ? 1 : w;
 }
 
-template <class Core>
+template <class Core, bool APPEND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Core::kWavesPerSimd)))
 void decode_balanced_kernel(DecodeParams a) {
   constexpr int B = Core::kBlock, D = Core::kHeadDim, G = Core::kGroup, ROW = Core::ROW;
@@ -830,8 +895,7 @@ void decode_balanced_kernel(DecodeParams a) {
     const int s_hi = min(a.S, s_lo + per);
     int local = 0, local_c = 0;
     for (int s = s_lo; s < s_hi; ++s) {
-      const int L = a.lens[s];
-      const int Lv = (L > 0 && L <= a.max_len) ? L : 0;
+      const int Lv = max(attended_len(a, s), 0);
       slen[s] = Lv;
       const int n = (Lv + kChunk - 1) / kChunk;
       local += n;
@@ -892,7 +956,7 @@ void decode_balanced_kernel(DecodeParams a) {
   if (worker >= W_eff) return;
   const int hsub = HG == 1 ? 0 : wave;                  // head of the group this wave takes
   // Shares are equal in cost: a segment costs its chunks plus kSegCost for
-  // its start (query fetch, table window, piece write).  chunk_at maps a
+  // its start (query fetch, table entries, piece write).  chunk_at maps a
   // cost position to the first chunk at or after it.
   const long long TC = (long long)NGR * uniform(pcost[a.S]);
   auto chunk_at = [&](long long x) -> long long {
@@ -952,12 +1016,10 @@ void decode_balanced_kernel(DecodeParams a) {
   const uint32_t rs = (uint32_t)Hkv * ROW;  // bytes between slots of one head
   const char* kpool = static_cast<const char*>(a.k);
   const char* vpool = static_cast<const char*>(a.v);
+  char* kpool_w = static_cast<char*>(const_cast<void*>(a.k));  // fused append writes
+  char* vpool_w = static_cast<char*>(const_cast<void*>(a.v));
   Core core;
   core.init(lane, rs, s_stage[wave]);
-
-  // Block-table window of the issue cursor's sequence.
-  int tw_s = -1, tw_base = 0, tbl = 0;
-  bool tw_bad = false;
 
   // Software pipeline of depth NB: the loads of the next NB-1 chunks are in
   // flight while a chunk is consumed.  Every step issues the same load
@@ -966,11 +1028,66 @@ void decode_balanced_kernel(DecodeParams a) {
   // consumed chunk's loads.  A chunk that opens a segment (or the wave's
   // first chunk) also brings the segment's query rows, loaded before the
   // chunk's rows.
+  //
+  // Block-table entries are read NB issues ahead: each pipeline slot also
+  // loads the entry of the chunk that will be issued into it next (a
+  // lookahead cursor runs NB chunks ahead of the issue cursor), and that
+  // entry is used only after the slot's own chunk has been consumed, that is
+  // after the wait that covers it.  A table read at the point of use would
+  // have to wait for every load in flight (the memory counter is in order),
+  // emptying the pipeline at each new sequence.
+  //
+  // With the fused append (APPEND), the same lookahead writes the new rows:
+  // when the lookahead chunk begins a segment whose last chunk lies in this
+  // share, the slot also loads that segment's new K and V row and the table
+  // entry of the row's block, and the wave stores the row right after it has
+  // consumed the slot's chunk, before it issues any chunk of that segment.  A
+  // wave's memory operations on one address take effect in program order, so
+  // the segment's loads see the new row; only this wave reads it.  The rows of
+  // segments met within the first NB chunks are written before the first
+  // issue.
   constexpr int NB = Core::kPipeline;
   long long to_issue = hi - lo, to_consume = hi - lo;
   typename Core::Buf buf[NB];
   bool bad[NB];
   bool first_issue = true;
+  Cursor la = ic;        // lookahead cursor
+  long long la_pos = lo; // chunk index of la
+  auto next_entry = [&](AppendSlot& sl) {
+    sl.off = -1;
+    if (la_pos >= hi) return;
+    sl.nid = a.tables[(size_t)la.s * a.MB + (la.j * kChunk) / B];
+    if constexpr (APPEND) {
+      if ((la.j == 0 || la_pos == lo) && la_pos + (la.n - 1 - la.j) < hi) {
+        const int p = la.L - 1;  // the appended position
+        const int head = la.g * HG + hsub;
+        sl.row = load_new_row<ROW>(a, B, la.s, head, p, lane);
+        sl.off = ((long long)(p % B) * Hkv + head) * ROW;
+      }
+    }
+    if (++la_pos < hi) advance(la);
+  };
+  auto commit = [&](AppendSlot& sl) {
+    if constexpr (APPEND) {
+      if (sl.off >= 0) {
+        const int blk = uniform(sl.row.blk);
+        if (blk >= 0 && blk < a.NB && lane < ROW / 16) {  // an id outside the pool writes nothing
+          const size_t d = (size_t)blk * B * rs + (size_t)sl.off + (size_t)lane * 16;
+          *reinterpret_cast<uint4*>(kpool_w + d) = sl.row.k;
+          *reinterpret_cast<uint4*>(vpool_w + d) = sl.row.v;
+        }
+        sl.off = -1;
+      }
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    buf[k].app.nid = 0;
+    next_entry(buf[k].app);  // entries (and rows) of the first NB chunks
+  }
+#pragma unroll
+  for (int k = 0; k < NB; ++k) commit(buf[k].app);
+
   auto issue_next = [&](typename Core::Buf& b, bool& bbad) {
     const char* kc = kpool;
     const char* vc = vpool;
@@ -980,20 +1097,15 @@ void decode_balanced_kernel(DecodeParams a) {
       if (first_issue || ic.j == 0) core.fetch_q(a, ic.s, ic.g * HG + hsub, b);
       first_issue = false;
       const int cs = ic.j * kChunk;
-      const int bi = cs / B;
-      if (ic.s != tw_s || bi < tw_base || bi >= tw_base + 64) {
-        tw_s = ic.s;
-        tw_base = bi & ~63;
-        tw_bad = false;
-        const int n_blk = (ic.L + B - 1) / B;
-        tbl = load_table_window(a.tables + (size_t)ic.s * a.MB, tw_base, n_blk, lane, a.NB, &tw_bad);
-      }
-      bbad = tw_bad;
-      const int phys = __builtin_amdgcn_readlane(tbl, bi - tw_base);
-      const size_t cbase = ((size_t)phys * B + (size_t)(cs % B)) * rs + (size_t)(ic.g * HG + hsub) * ROW;
+      const int id = uniform(b.app.nid);      // this chunk's table entry, loaded NB issues ago
+      const bool ok = id >= 0 && id < a.NB;   // an id outside the pool is never dereferenced
+      bbad = !ok;
+      const size_t cbase =
+          ((size_t)(ok ? id : 0) * B + (size_t)(cs % B)) * rs + (size_t)(ic.g * HG + hsub) * ROW;
       kc = kpool + cbase;
       vc = vpool + cbase;
-      nbytes = (uint32_t)min(kChunk - 1, ic.L - 1 - cs) * rs + ROW;  // rows 0 .. lim of this head
+      nbytes = ok ? (uint32_t)min(kChunk - 1, ic.L - 1 - cs) * rs + ROW : 0u;  // rows 0 .. lim of this head
+      next_entry(b.app);  // for the chunk issued into this slot next
       --to_issue;
       if (to_issue > 0) advance(ic);
     }
@@ -1004,7 +1116,8 @@ void decode_balanced_kernel(DecodeParams a) {
   bool seg_bad = false;
   bool first_consume = true;
   // One step: issue into the slot consumed one step earlier, consume the
-  // current chunk, close the segment piece if it ends here, step the cursor.
+  // current chunk, write the new row the slot brought, close the segment
+  // piece if it ends here, step the cursor.
   auto step = [&](typename Core::Buf& cur, bool curbad, typename Core::Buf& nxt, bool& nxtbad) {
     issue_next(nxt, nxtbad);
     if (to_consume <= 0) return;
@@ -1016,6 +1129,7 @@ void decode_balanced_kernel(DecodeParams a) {
       first_consume = false;
     }
     core.consume(min(kChunk - 1, cc.L - 1 - cc.j * kChunk), a.scale_log2, cur);
+    commit(cur.app);
     seg_bad |= curbad;
     --to_consume;
     const bool seg_end = (cc.j == cc.n - 1);
@@ -1057,9 +1171,9 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(Decode
   if (seg >= a.S * a.Hkv) return;
   const int s = seg / a.Hkv;
   const int g = seg - s * a.Hkv;
-  const int L = a.lens[s];
+  const int L = attended_len(a, s);
   float* o0 = a.out + ((size_t)s * a.Hq + (size_t)g * G) * D + lane * CPL;  // row h at o0 + h * D
-  if (L < 0 || L > a.max_len || L == 0) {
+  if (L <= 0) {
     const float fill = L == 0 ? 0.0f : __builtin_nanf("");
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -1151,9 +1265,9 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_wide_kernel(D
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int L = a.lens[s];
+  const int L = attended_len(a, s);
   float* orow = a.out + (size_t)row * D;
-  if (L < 0 || L > a.max_len || L == 0) {
+  if (L <= 0) {
     const float fill = L == 0 ? 0.0f : __builtin_nanf("");
     for (int i = tid; i < D; i += kThreads) orow[i] = fill;
     return;
@@ -1238,7 +1352,10 @@ hipError_t launch_stage1(const DecodeParams& p, hipStream_t stream) {
   const dim3 block(kThreads);
   if (p.schedule == kBalanced) {
     const size_t lds = (size_t)(3 * p.S + 2) * sizeof(int);
-    hipLaunchKernelGGL((decode_balanced_kernel<Core>), grid, block, lds, stream, p);
+    if (p.append)
+      hipLaunchKernelGGL((decode_balanced_kernel<Core, true>), grid, block, lds, stream, p);
+    else
+      hipLaunchKernelGGL((decode_balanced_kernel<Core, false>), grid, block, lds, stream, p);
   } else {
     hipLaunchKernelGGL((decode_partitioned_kernel<Core>), grid, block, 0, stream, p);
   }

@@ -137,6 +137,9 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   p->v = v_cache;
   p->tables = block_tables;
   p->lens = context_lens;
+  p->k_new = nullptr;
+  p->v_new = nullptr;
+  p->append = 0;
   p->S = num_seqs;
   p->Hq = q_heads;
   p->Hkv = kv_heads;
@@ -419,6 +422,74 @@ int paged_attn_decode(float* out, const void* q, const void* k_cache, const void
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads, s);
   if (e == hipSuccess) e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, s);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// The fused append: the same plan and checks as the decode of L + 1 tokens,
+// plus the new rows.
+static int prepare_decode_append(float* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                 const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                 int32_t max_context_len, float scale, int32_t dtype, int32_t partition_size,
+                                 void* workspace, size_t workspace_bytes, pkv::DecodeParams* p) {
+  const int st = prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, q_heads, kv_heads,
+                                head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                                partition_size, workspace, workspace_bytes, p);
+  if (st != PKV_OK) return st;
+  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+  p->k_new = k_new;
+  p->v_new = v_new;
+  p->append = 1;
+  return PKV_OK;
+}
+
+int paged_attn_decode_append(float* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                             const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, float scale, int32_t dtype, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::DecodeParams p;
+  const int st = prepare_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, num_seqs,
+                                       q_heads, kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                       max_context_len, scale, dtype, partition_size, workspace, workspace_bytes, &p);
+  if (st != PKV_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads, s);
+  if (e == hipSuccess) e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, s);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int paged_attn_decode_append_partitions(float* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                        const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                        int32_t max_context_len, float scale, int32_t dtype,
+                                        int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  pkv::DecodeParams p;
+  const int st = prepare_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, num_seqs,
+                                       q_heads, kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                       max_context_len, scale, dtype, partition_size, workspace, workspace_bytes, &p);
+  if (st != PKV_OK) return st;
+  const hipError_t e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads,
+                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int paged_attn_decode_append_reduce(float* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                    const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                    int32_t max_context_len, float scale, int32_t dtype, int32_t partition_size,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::DecodeParams p;
+  const int st = prepare_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, num_seqs,
+                                       q_heads, kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                       max_context_len, scale, dtype, partition_size, workspace, workspace_bytes, &p);
+  if (st != PKV_OK) return st;
+  const hipError_t e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

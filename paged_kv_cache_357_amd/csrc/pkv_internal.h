@@ -69,6 +69,9 @@ struct DecodeParams {
   const void* v;          // [NB, B, Hkv, D]
   const int32_t* tables;  // [S, MB]
   const int32_t* lens;    // [S]
+  const void* k_new;      // fused append: [S, Hkv, D] rows written at position lens[s]; else null
+  const void* v_new;
+  int32_t append;         // 1: lens hold the lengths before the fused append, L + 1 tokens are attended
   int32_t S, Hq, Hkv, NB, MB, max_len;
   int32_t schedule;       // Schedule
   int32_t P, NP;          // partitioned: partition size and count

@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 28, names
+    assert len(names) == 31, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -106,6 +106,25 @@ def test_decode_rejects_before_launch(lib):
     assert f(*_decode_args(**ptrs, maxL=40, P=16, ws=fake, wsb=16)) == -5
     assert lib.paged_attn_decode_partitions(*_decode_args()) == -1
     assert lib.paged_attn_decode_reduce(*_decode_args(**ptrs, dtype=5)) == -3
+
+
+def test_decode_append_rejects_before_launch(lib):
+    fake = 0x1000  # never dereferenced: every call below fails its host checks
+    ptrs = dict(out=fake, q=fake, k=fake, v=fake, t=fake, lens=fake)
+
+    def args(k_new=fake, v_new=fake, **kw):
+        a = _decode_args(**kw)
+        return a[:4] + [k_new, v_new] + a[4:]
+
+    for f in (lib.paged_attn_decode_append, lib.paged_attn_decode_append_partitions,
+              lib.paged_attn_decode_append_reduce):
+        assert f(*args(None, None)) == -1                                 # null pointers
+        assert f(*args(None, fake, **ptrs)) == -1                         # no k_new
+        assert f(*args(fake, None, **ptrs)) == -1                         # no v_new
+        assert f(*args(**ptrs, maxL=49)) == -2                            # > MB * B
+        assert f(*args(**ptrs, dtype=5)) == -3
+        assert f(*args(**ptrs, maxL=40, P=16)) == -5                      # needs workspace
+        assert f(*args(None, None, S=0)) == 0                             # nothing to do
 
 
 def test_append_and_slot_mapping_reject(lib):
