@@ -876,7 +876,8 @@ template <class Core, bool APPEND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Core::kWavesPerSimd)))
 void decode_balanced_kernel(DecodeParams a) {
   constexpr int B = Core::kBlock, D = Core::kHeadDim, G = Core::kGroup, ROW = Core::ROW;
-  extern __shared__ int smem[];
+  constexpr int REC = piece_record_bytes(G, D);
+  extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ __attribute__((aligned(16))) char s_stage[kWavesPerWG][Core::kStageBytes];
   int* pref = smem;               // [S + 1] chunk prefix sums C_s
   int* slen = smem + a.S + 1;     // [S] lengths (0 for invalid ones)
@@ -1112,12 +1113,38 @@ void decode_balanced_kernel(DecodeParams a) {
     core.issue(kc, vc, rs, nbytes, b);
   };
 
+  // Finished pieces wait in this wave's LDS queue and are written out after
+  // its last chunk (or when the queue is full).  The memory counter is in
+  // order and counts stores too, so a store issued amid the stream would
+  // hold up the wait for every chunk issued after it until the store is
+  // acknowledged, which under a full read stream takes longer than a load.
+  // A record: global destinations of the rows and of the (max, sum) pairs
+  // (0: none), then G * D floats, then G pairs.
+  char* queue = reinterpret_cast<char*>(smem + ((3 * a.S + 2 + 3) & ~3)) + (size_t)wave * a.queue_bytes;
+  const int q_cap = a.queue_bytes / REC;  // at least one (the plan sees to it)
+  int q_n = 0;
+  auto flush = [&]() {
+    for (int r = 0; r < q_n; ++r) {
+      const char* rec = queue + r * REC;
+      const uint64_t gd = *reinterpret_cast<const uint64_t*>(rec);
+      const uint64_t gm = *reinterpret_cast<const uint64_t*>(rec + 8);
+      typedef __attribute__((address_space(1))) f32x4 g_f32x4;  // global memory
+      typedef __attribute__((address_space(1))) u32x2 g_u32x2;
+      g_f32x4* dst = (g_f32x4*)(
+          ((uint64_t)(uint32_t)uniform((int)(uint32_t)(gd >> 32)) << 32) | (uint32_t)uniform((int)(uint32_t)gd));
+      const f32x4* src = reinterpret_cast<const f32x4*>(rec + 16);
+      for (int i = lane; i < G * D / 4; i += 64) dst[i] = src[i];
+      if (gm != 0 && lane < G) ((g_u32x2*)gm)[lane] = reinterpret_cast<const u32x2*>(rec + 16 + 4 * G * D)[lane];
+    }
+    q_n = 0;
+  };
+
   bool started = false;
   bool seg_bad = false;
   bool first_consume = true;
   // One step: issue into the slot consumed one step earlier, consume the
   // current chunk, write the new row the slot brought, close the segment
-  // piece if it ends here, step the cursor.
+  // piece if it ends here (into the queue), step the cursor.
   auto step = [&](typename Core::Buf& cur, bool curbad, typename Core::Buf& nxt, bool& nxtbad) {
     issue_next(nxt, nxtbad);
     if (to_consume <= 0) return;
@@ -1134,16 +1161,25 @@ void decode_balanced_kernel(DecodeParams a) {
     --to_consume;
     const bool seg_end = (cc.j == cc.n - 1);
     if (seg_end || to_consume == 0) {
+      if (q_n == q_cap) flush();
+      char* rec = queue + q_n * REC;
       PieceSink o;
       o.direct = started && seg_end;
       o.bad = seg_bad;
-      o.out = a.out + ((size_t)cc.s * a.Hq + (size_t)(cc.g * HG + hsub) * G) * D;
-      const size_t r0 = ((size_t)w * 2 + (started ? 1 : 0)) * G;
-      o.acc = a.ws_acc + r0 * D;
+      o.out = reinterpret_cast<float*>(rec + 16);  // G rows of D, then G pairs
+      o.acc = o.out;
       o.acc_stride = 1;
-      o.ml = a.ws_ml + r0;
+      o.ml = reinterpret_cast<float2*>(rec + 16 + 4 * G * D);
       o.ml_stride = 1;
+      if (lane == 0) {
+        const size_t r0 = ((size_t)w * 2 + (started ? 1 : 0)) * G;
+        float* rows = o.direct ? a.out + ((size_t)cc.s * a.Hq + (size_t)(cc.g * HG + hsub) * G) * D
+                               : a.ws_acc + r0 * D;
+        reinterpret_cast<uint64_t*>(rec)[0] = reinterpret_cast<uint64_t>(rows);
+        reinterpret_cast<uint64_t*>(rec)[1] = o.direct ? 0 : reinterpret_cast<uint64_t>(a.ws_ml + r0);
+      }
       core.finish(o);
+      ++q_n;
     }
     if (to_consume > 0) advance(cc);
   };
@@ -1154,6 +1190,7 @@ void decode_balanced_kernel(DecodeParams a) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) step(buf[k], bad[k], buf[(k + NB - 1) % NB], bad[(k + NB - 1) % NB]);
   }
+  flush();
 }
 
 // Stage 2 of the balanced schedule: one wave per segment (s, g), taking the
@@ -1348,10 +1385,11 @@ using CoreFor = typename std::conditional<(DT == 1 && G >= kMfmaMinGroup), MfmaC
 template <int DT, int D, int B, int G>
 hipError_t launch_stage1(const DecodeParams& p, hipStream_t stream) {
   using Core = CoreFor<DT, D, B, G>;
+  static_assert(Core::kStageBytes == balanced_stage_bytes(DT, D, G), "the plan's LDS estimate must match the core");
   const dim3 grid(p.grid);
   const dim3 block(kThreads);
   if (p.schedule == kBalanced) {
-    const size_t lds = (size_t)(3 * p.S + 2) * sizeof(int);
+    const size_t lds = (((size_t)(3 * p.S + 2) + 3) & ~(size_t)3) * sizeof(int) + (size_t)kWavesPerWG * p.queue_bytes;
     if (p.append)
       hipLaunchKernelGGL((decode_balanced_kernel<Core, true>), grid, block, lds, stream, p);
     else

@@ -27,6 +27,7 @@ struct Plan {
   int xcd_group = 0;
   int head_group = 1;
   int grid = 0;
+  int queue_bytes = 0;   // balanced: LDS queue of finished pieces per wave
   size_t acc_bytes = 0;  // workspace region of partial accumulators
   size_t ml_bytes = 0;   // workspace region of partial (max, sum) pairs
   size_t pref_bytes = 0; // workspace region of per-sequence chunk and cost prefix sums (balanced)
@@ -71,13 +72,23 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
   // products with the worker count stay within 62 bits.
   const long long chunk_bound = (long long)num_seqs * kv_heads * ((max_context_len + pkv::kChunk - 1) / pkv::kChunk);
   const bool spills = dtype == PKV_DTYPE_F32 && head_dim == 128 && group == 16;  // one wave per SIMD is not enough
+  // Each wave keeps its finished pieces in an LDS queue and writes them out
+  // at its end; the queue takes what the prefix tables and staging tiles
+  // leave of the LDS budget, and must hold at least one piece.
+  const long long lds_fixed = round_up((3 * (size_t)num_seqs + 2) * 4, 16) +
+                              (long long)pkv::kWavesPerWG * pkv::balanced_stage_bytes(dtype, head_dim, group) + 256;
+  long long queue = (pkv::kLdsBudget - lds_fixed) / pkv::kWavesPerWG;
+  if (queue > pkv::kQueueMaxBytes) queue = pkv::kQueueMaxBytes;
+  queue &= ~15LL;
+  const bool queue_fits = queue >= pkv::piece_record_bytes(group, head_dim);
   if (partition_size == 0 && max_context_len > kAutoPartition && num_seqs <= pkv::kBalancedMaxSeqs &&
-      chunk_bound < (1LL << 48) && !spills) {
+      chunk_bound < (1LL << 48) && !spills && queue_fits) {
     const long long waves =
         (long long)pkv::kCUs * pkv::kSimdsPerCU * pkv::balanced_waves_per_simd(dtype, head_dim, group);
     plan->schedule = pkv::kBalanced;
     plan->P = 0;
     plan->NP = 0;
+    plan->queue_bytes = (int)queue;
     // matrix-core kernels: four waves of a workgroup on four adjacent heads
     plan->head_group = (dtype == PKV_DTYPE_BF16 && group >= pkv::kMfmaMinGroup && kv_heads % 4 == 0) ? 4 : 1;
     plan->n_units = (int)waves;
@@ -153,6 +164,7 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   p->xcd_group = plan.xcd_group;
   p->head_group = plan.head_group;
   p->grid = plan.grid;
+  p->queue_bytes = plan.queue_bytes;
   p->scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   return PKV_OK;
 }

@@ -54,6 +54,22 @@ constexpr __host__ __device__ int balanced_pipeline_depth(int dtype, int head_di
   return (dtype == 0 && (group >= 4 || (head_dim == 128 && group >= 2))) ? 2 : PKV_PIPELINE;
 }
 
+// LDS one balanced-schedule workgroup may use (prefix tables, K staging
+// tiles, finished-piece queues), and the most any wave's queue takes.
+constexpr int kLdsBudget = 64 * 1024;
+constexpr int kQueueMaxBytes = 16 * 1024;
+// Bytes of one queued finished piece: a 16-byte header (global destinations
+// of the rows and of the (max, sum) pairs), group * head_dim floats, group
+// (max, sum) pairs; a multiple of 16.
+constexpr __host__ __device__ int piece_record_bytes(int group, int head_dim) {
+  return (16 + 4 * group * head_dim + 8 * group + 15) & ~15;
+}
+// Per-wave LDS tile of the balanced stage-1 core (the matrix-core core stages
+// a chunk's K rows, the vector core none).
+constexpr __host__ __device__ int balanced_stage_bytes(int dtype, int head_dim, int group) {
+  return (dtype == 1 && group >= kMfmaMinGroup) ? kChunk * head_dim * 2 : 16;
+}
+
 enum Schedule : int32_t {
   kPartitioned = 0,  // one wave per (partition, sequence, kv head)
   kBalanced = 1      // equal shares of all chunks, one share per resident wave
@@ -80,6 +96,7 @@ struct DecodeParams {
   int32_t xcd_group;      // consecutive logical workgroups kept on one XCD (0: no remap)
   int32_t head_group;     // balanced: adjacent kv heads the waves of a workgroup take in lockstep (1 or 4)
   int32_t grid;           // launched workgroups (>= n_wg; the surplus exits at once)
+  int32_t queue_bytes;    // balanced: LDS bytes of each wave's finished-piece queue (>= one record)
   float scale_log2;       // scale * log2(e): scores live in the base-2 domain
 };
 
