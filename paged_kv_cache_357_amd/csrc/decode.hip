@@ -1193,8 +1193,8 @@ void decode_balanced_kernel(DecodeParams a) {
   flush();
 }
 
-// Stage 2 of the balanced schedule: one wave per segment (s, g), taking the
-// G query-head rows h of kv head g in turn, four segments per workgroup.  An
+// Stage 2 of the balanced schedule: one wave per segment (s, g), merging the
+// G query-head rows h of kv head g together, four segments per workgroup.  An
 // invalid length gives NaN rows and L = 0 zeros; a segment that one wave
 // finished was written by stage 1; otherwise the pieces of waves w0 .. w1
 // (slot 1 of w0, slot 0 of the later ones) are merged in wave order:
@@ -1203,12 +1203,19 @@ void decode_balanced_kernel(DecodeParams a) {
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(DecodeParams a) {
   constexpr int CPL = D / 64;  // columns per lane (1 or 2)
+  // Pieces whose records are loaded together (registers: KB * G * (CPL + 2)).
+  constexpr int KB = G <= 1 ? 8 : (G <= 2 ? 4 : (G <= 4 ? 2 : 1));
   const int lane = threadIdx.x & 63;
   const int seg = blockIdx.x * kWavesPerWG + uniform(threadIdx.x >> 6);  // s * Hkv + kv head
   if (seg >= a.S * a.Hkv) return;
   const int s = seg / a.Hkv;
   const int g = seg - s * a.Hkv;
+  // Everything that depends on s alone is loaded before anything is decided,
+  // so the loads are in flight together.
   const int L = attended_len(a, s);
+  const int pref_S = a.ws_pref[a.S];
+  const int cost_S = a.ws_pref[a.S + 1 + a.S];
+  const int cost_s = a.ws_pref[a.S + 1 + s];
   float* o0 = a.out + ((size_t)s * a.Hq + (size_t)g * G) * D + lane * CPL;  // row h at o0 + h * D
   if (L <= 0) {
     const float fill = L == 0 ? 0.0f : __builtin_nanf("");
@@ -1220,11 +1227,11 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(Decode
   }
   const int HG = a.head_group;
   const int NGR = a.Hkv / HG;
-  const long long T = (long long)NGR * a.ws_pref[a.S];
+  const long long T = (long long)NGR * pref_S;
   const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
   const int n = (L + kChunk - 1) / kChunk;
-  const long long TC = (long long)NGR * a.ws_pref[a.S + 1 + a.S];
-  const long long cbase = (long long)NGR * a.ws_pref[a.S + 1 + s] + (long long)(g / HG) * (n + kSegCost) + kSegCost;
+  const long long TC = (long long)NGR * cost_S;
+  const long long cbase = (long long)NGR * cost_s + (long long)(g / HG) * (n + kSegCost) + kSegCost;
   const long long w0 = balanced_wave_of(cbase, TC, W_eff);  // first and last worker of the segment
   const long long w1 = balanced_wave_of(cbase + n - 1, TC, W_eff);
   const int hsub = g % HG;
@@ -1235,40 +1242,57 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(Decode
     return (wave_id * 2 + (p == 0 ? 1 : 0)) * G;
   };
 
-  float M[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) M[h] = kNegBig;
-  for (int p = lane; p < k; p += 64) {
-    const size_t r = piece_row(p);
-#pragma unroll
-    for (int h = 0; h < G; ++h) M[h] = fmaxf(M[h], a.ws_ml[r + h].x);
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M[h] = fmaxf(M[h], __shfl_xor(M[h], off));
-
-  float num[G][CPL], den[G];
+  // Pieces in wave order, KB at a time: M is the largest max so far, and a
+  // later batch with a larger one rescales the sums.  With k <= KB this is
+  // one batch: M over all pieces, then the sums in piece order.
+  float M[G], num[G][CPL], den[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    M[h] = kNegBig;
     den[h] = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) num[h][j] = 0.0f;
   }
-  // pieces in wave order; the G rows of a piece are loaded together
-  for (int p = 0; p < k; ++p) {
-    const size_t r = piece_row(p);
+  for (int p0 = 0; p0 < k; p0 += KB) {
+    float2 t[KB][G];
+    float x[KB][G][CPL];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const bool in = p0 + i < k;
+      const size_t r = piece_row(in ? p0 + i : p0);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        t[i][h] = in ? a.ws_ml[r + h] : make_float2(kNegBig, 0.0f);
+        if constexpr (CPL == 2) {
+          const float2 v = in ? *reinterpret_cast<const float2*>(a.ws_acc + (r + h) * D + lane * CPL)
+                              : make_float2(0.0f, 0.0f);
+          x[i][h][0] = v.x;
+          x[i][h][1] = v.y;
+        } else {
+          x[i][h][0] = in ? a.ws_acc[(r + h) * D + lane] : 0.0f;
+        }
+      }
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float2 t = a.ws_ml[r + h];
-      const float f = fast_exp2(t.x - M[h]);
-      den[h] = fmaf(t.y, f, den[h]);
-      if constexpr (CPL == 2) {
-        const float2 x = *reinterpret_cast<const float2*>(a.ws_acc + (r + h) * D + lane * CPL);
-        num[h][0] = fmaf(x.x, f, num[h][0]);
-        num[h][1] = fmaf(x.y, f, num[h][1]);
-      } else {
-        num[h][0] = fmaf(a.ws_acc[(r + h) * D + lane], f, num[h][0]);
+      float Mn = M[h];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) Mn = fmaxf(Mn, t[i][h].x);
+      if (p0 > 0) {
+        const float sc = fast_exp2(M[h] - Mn);
+        den[h] *= sc;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) num[h][j] *= sc;
+      }
+      M[h] = Mn;
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        if (p0 + i < k) {
+          const float f = fast_exp2(t[i][h].x - M[h]);
+          den[h] = fmaf(t[i][h].y, f, den[h]);
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) num[h][j] = fmaf(x[i][h][j], f, num[h][j]);
+        }
       }
     }
   }

@@ -143,3 +143,34 @@ def test_balanced_and_partitioned_agree(pk):
     assert_parity(a, ref, w, what="balanced")
     assert_parity(b, ref, w, what="partitioned")
     assert float(np.max(np.abs(a.astype(np.float64) - b))) <= 2 * TOL[w.dtype]
+
+
+@pytest.mark.parametrize("case", ["g16-one-record", "g1-many-segments"])
+def test_piece_queue_flushes_mid_stream(pk, case):
+    """Each wave keeps its finished pieces in an LDS queue and writes them out
+    at its end, or when the queue is full.  Group 16 at head_dim 128 leaves
+    room for one record per wave (every piece after the first flushes the
+    queue); 2048 short sequences with 16 kv heads give each wave about 32
+    pieces against a queue of 18.  Every row is compared with the
+    partitioned schedule, and a sample with the oracle."""
+    rng = np.random.default_rng(358777 if case.startswith("g16") else 358778)
+    if case == "g16-one-record":
+        lens = rng.integers(1, 41, size=600)
+        lens[17] = 700
+        w = make_workload("queue-g16", lens, 32, 2, 128, 16, "bf16", 358779)
+    else:
+        lens = rng.integers(1, 25, size=2048)
+        lens[1000] = 600
+        w = make_workload("queue-g1", lens, 16, 16, 128, 16, "bf16", 358780)
+    _assert_balanced(pk, w)
+    d = to_gpu(w)
+    say(f"{case}: S={w.num_seqs} G={w.group} sum L={int(w.context_lens.sum())}")
+    out = gpu_decode(pk, w, d)
+    part = gpu_decode(pk, w, d, partition_size=512)
+    e = float(np.max(np.abs(out.astype(np.float64) - part)))
+    say(f"{case}: max|balanced - partitioned| = {e:.3e}")
+    assert np.all(np.isfinite(out)) and e <= TOL[w.dtype]
+    seqs = sorted(set(range(0, w.num_seqs, max(1, w.num_seqs // 40))) | {17 if case.startswith("g16") else 1000,
+                                                                          w.num_seqs - 1})
+    ref = oracle_out(w, seqs=seqs)
+    assert_parity(out, ref, w, seqs=seqs, what="queued pieces")
