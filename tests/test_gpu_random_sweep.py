@@ -55,3 +55,30 @@ def test_random_config_matches_oracle(pk, i):
     out = gpu_decode(pk, w, d, partition_size=c["P"], max_len=max(1, w.max_context_len))
     ref = oracle_out(w)
     assert_parity(out, ref, w, what=f"sweep case {i}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_config_fused_append_matches_oracle(pk, i):
+    """The same random configurations through paged_attn_decode_append: each
+    sequence's new row lands at position L (pools bit for bit against the
+    oracle's own slot computation) and the decode over L + 1 tokens matches
+    the oracle on the appended pools."""
+    import oracle.paged_attention as pa
+    from workloads import raw_numpy
+    c = _case(100 + i)
+    w = make_workload(f"sweep-fused-{i}", c["lens"], c["G"] * c["hkv"], c["hkv"], c["D"], c["B"], c["dtype"],
+                      9990 + i)
+    dt = pk.DTYPE_BF16 if c["dtype"] == "bf16" else pk.DTYPE_F32
+    max_len = w.max_context_len + 1
+    plan = pk.plan(w.num_seqs, w.q_heads, w.kv_heads, w.head_dim, w.block_size, max_len, dt, c["P"])
+    say(f"fused sweep {i}: {c['dtype']} D={c['D']} B={c['B']} G={c['G']} Hkv={c['hkv']} S={w.num_seqs} "
+        f"max L+1={max_len} P={c['P']} plan={plan}")
+    d = to_gpu(w)
+    out = pk.decode_append(d.q, d.k, d.v, d.kn, d.vn, d.tables, d.lens, w.scale, max_len, c["P"])
+    torch.cuda.synchronize()
+    k2, v2 = pa.oracle_append(raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables, w.context_lens,
+                              raw_numpy(w.k_new), raw_numpy(w.v_new), w.block_size)
+    assert np.array_equal(raw_numpy(d.k.cpu()).view(np.uint8), k2.view(np.uint8)), "K pool differs"
+    assert np.array_equal(raw_numpy(d.v.cpu()).view(np.uint8), v2.view(np.uint8)), "V pool differs"
+    ref = oracle_out(w, lens=w.context_lens + 1, k_cache=k2, v_cache=v2)
+    assert_parity(out.cpu().numpy(), ref, w, what=f"fused sweep case {i}")
