@@ -3,9 +3,10 @@
 A step is the whole path over one batch: slot mapping for every sequence's
 new token and the K/V append into its block, the fused score / online-softmax /
 V pass over every sequence's physical blocks (stage 1), and the merge of the
-pieces of split segments (stage 2).  By default the append is a launch of its
-own before stage 1; --fused-append runs paged_attn_decode_append instead,
-where stage 1 writes the new rows itself.  The
+pieces of split segments (stage 2), run as one paged_attn_decode_append call:
+with the vector-ALU kernels stage 1 writes the new rows itself, with the
+matrix-core kernels the call writes them in a launch of its own first.
+--two-launch runs paged_kv_append_at and then paged_attn_decode instead.  The
 workload is the Llama-7B-shaped decode batch (64 sequences, context lengths
 uniform in [128, 2048], 32 query / 32 kv heads, head_dim 128, bf16 K/V in
 16-token blocks dealt from a shuffled pool 1.25x the blocks in use).  Each
@@ -70,8 +71,8 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--deal", default="shuffled", choices=["shuffled", "identity"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fused-append", action="store_true",
-                    help="fuse the append into stage 1 (paged_attn_decode_append) instead of its own launch")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="run the append as its own launch (paged_kv_append_at), then paged_attn_decode")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = all)")
     ap.add_argument("--probes", action="store_true", help="also time plain HBM read / copy probes")
     ap.add_argument("--flush-reps", type=int, default=0,
@@ -332,7 +333,7 @@ def main():
     lens = torch.from_numpy(lens_step).to(dev)
     max_len = int(lens_step.max())
     slots = torch.empty(w.num_seqs, dtype=torch.int32, device=dev)
-    two_launch = not args.fused_append
+    two_launch = args.two_launch
     if two_launch:
         # slot mapping + K/V append in a launch of its own, then the decode of L + 1
         call = pk.DecodeCall(q, kc, vc, tables, lens, w.scale, max_len, args.partition_size)
@@ -408,7 +409,7 @@ def main():
         "partition_kernel_ms": part_ms, "partition_kernel_samples": len(sampled),
         "reduce_kernel_ms_untimed": red_ms,
         "append_at_kernel_ms_untimed": app_ms,
-        "append": "separate launch (append_at)" if two_launch else "fused into stage 1",
+        "append": "separate launch (append_at)" if two_launch else "paged_attn_decode_append",
         "schedule": "balanced" if balanced else "partitioned",
         "partition_size": P, "num_partitions": NP,
         "kernel_sha": kernel_sha(),

@@ -225,8 +225,12 @@ PKV_API int paged_attn_decode_reduce(float* out, const void* q, const void* k_ca
  *   out[s,h,:] = paged_attn_decode over positions 0 .. L
  *
  * The result equals paged_kv_append_at(positions = context_lens) followed by
- * paged_attn_decode with context_lens + 1, bitwise, in one launch fewer: the
- * wave that streams the chunk holding position L writes the new row first.
+ * paged_attn_decode with context_lens + 1, bitwise.  With the vector-ALU
+ * kernels (fp32, or bf16 with fewer than 4 query heads per kv head) under
+ * the balanced schedule, and with the partitioned schedule, stage 1 writes
+ * the new rows itself, one launch fewer; with the matrix-core kernels the
+ * call writes them with a launch of its own before stage 1 (measured
+ * faster for those kernels).
  *
  *   k_cache, v_cache [num_blocks, block_size, kv_heads, head_dim] dtype, in/out:
  *                the new rows are written, nothing else.
@@ -243,7 +247,8 @@ PKV_API int paged_attn_decode_reduce(float* out, const void* q, const void* k_ca
  *   and must not lie in a block another sequence shares (copy-on-write first).
  *
  * Errors: those of paged_attn_decode; PKV_ERR_NULL also for a missing k_new
- * or v_new.  The _partitions / _reduce pair splits the call into its two
+ * or v_new; PKV_ERR_SHAPE also when num_blocks * block_size exceeds
+ * INT32_MAX (as for paged_kv_append_at).  The _partitions / _reduce pair splits the call into its two
  * stages like paged_attn_decode_partitions / _reduce (the append happens in
  * the first).
  */

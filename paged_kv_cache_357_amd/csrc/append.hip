@@ -54,21 +54,21 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ kc, char
 // Slot mapping and append in one pass: thread (t, c) computes the slot of
 // sequence t's position itself (every thread of the row gets the same value
 // from the same two loads), copies column c, and column 0 records the slot.
-// A position outside the table or a block id outside the pool gives slot -1
-// and no write.
+// A position outside [0, pos_end) (pos_end at most the table's extent) or a
+// block id outside the pool gives slot -1 and no write.
 __global__ __launch_bounds__(256) void append_at_kernel(char* __restrict__ kc, char* __restrict__ vc,
                                                         const char* __restrict__ kn, const char* __restrict__ vn,
                                                         const int32_t* __restrict__ tables,
                                                         const int32_t* __restrict__ positions,
                                                         int32_t* __restrict__ slots, int N, int MB, int B, int NB,
-                                                        int cols16) {
+                                                        int cols16, long long pos_end) {
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long t = gid / cols16;
   const int c = (int)(gid - t * cols16);
   if (t >= N) return;
   const int p = positions[t];
   int slot = -1;
-  if (p >= 0 && (long long)p < (long long)MB * B) {
+  if (p >= 0 && (long long)p < pos_end) {
     const int b = p / B;
     const int blk = tables[(size_t)t * MB + b];
     if (blk >= 0 && blk < NB) slot = blk * B + (p - b * B);
@@ -192,7 +192,7 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, 
 
 hipError_t launch_append_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* tables, const int32_t* positions, int32_t* slots, int N, int MB, int B,
-                            int NB, int row_bytes, hipStream_t stream) {
+                            int NB, int row_bytes, long long pos_end, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int cols16 = row_bytes / 16;
   const long long total = (long long)N * cols16;
@@ -200,7 +200,7 @@ hipError_t launch_append_at(void* k_cache, void* v_cache, const void* k_new, con
   const long long blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(append_at_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, static_cast<char*>(k_cache),
                      static_cast<char*>(v_cache), static_cast<const char*>(k_new), static_cast<const char*>(v_new),
-                     tables, positions, slots, N, MB, B, NB, cols16);
+                     tables, positions, slots, N, MB, B, NB, cols16, pos_end);
   return hipGetLastError();
 }
 

@@ -293,6 +293,22 @@ struct ValuCore {
       for (int i = 0; i < 4; ++i) q[h][i] = b.q[h][i];
   }
 
+  // Fused append: replace row lim of a loaded chunk (the slot of the new
+  // token, loaded before the new row is written) by the new K and V rows
+  // kept in LDS.  Row lim is row lim % TPI of load lim / TPI.
+  __device__ void substitute(int lim, Buf& b, const char* krow, const char* vrow) const {
+    const u32x4 nk = *reinterpret_cast<const u32x4*>(krow + seg * 16);
+    const u32x4 nv = *reinterpret_cast<const u32x4*>(vrow + seg * 16);
+    const bool mine = grp == lim % TPI;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (mine && i == lim / TPI) {
+        b.k[i] = nk;
+        b.v[i] = nv;
+      }
+    }
+  }
+
   // Loads of one chunk: kc / vc point at the chunk's first row of this kv
   // head; the buffer resources cover `nbytes` from there (rows 0 .. lim, or
   // nothing for a load-free dummy), so rows past the end read as zero.
@@ -529,6 +545,23 @@ struct MfmaCore {
   __device__ void take_q(const Buf& b) {
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) q[j] = b.q[j];
+  }
+
+  // Fused append: replace row lim of a loaded chunk by the new K and V rows
+  // kept in LDS, in the layouts of the K row loads (row lim is row lim % RPI
+  // of K load lim / RPI) and of the V operand (token slot lim is register
+  // lim % 4 of lane group lim / 4).
+  __device__ void substitute(int lim, Buf& b, const char* krow, const char* vrow) const {
+    const int lane = gl * 16 + cl;
+    const u32x4 nk = *reinterpret_cast<const u32x4*>(krow + (lane % LPR) * 16);
+    const VRow nv = *reinterpret_cast<const VRow*>(vrow + cl * (2 * CW));
+    const bool mine_k = lane / LPR == lim % RPI;
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      if (mine_k && i == lim / RPI) b.k[i] = nk;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * gl + r == lim) b.v[r] = nv;
   }
 
   __device__ void issue(const char* kc, const char* vc, uint32_t rs, uint32_t nbytes, Buf& b) const {
@@ -1038,15 +1071,19 @@ void decode_balanced_kernel(DecodeParams a) {
   // have to wait for every load in flight (the memory counter is in order),
   // emptying the pipeline at each new sequence.
   //
-  // With the fused append (APPEND), the same lookahead writes the new rows:
+  // With the fused append (APPEND), the same lookahead brings the new rows:
   // when the lookahead chunk begins a segment whose last chunk lies in this
   // share, the slot also loads that segment's new K and V row and the table
-  // entry of the row's block, and the wave stores the row right after it has
-  // consumed the slot's chunk, before it issues any chunk of that segment.  A
-  // wave's memory operations on one address take effect in program order, so
-  // the segment's loads see the new row; only this wave reads it.  The rows of
-  // segments met within the first NB chunks are written before the first
-  // issue.
+  // entry of the row's block.  After the slot's chunk is consumed the row
+  // goes into the wave's LDS row store; the segment's last chunk, which was
+  // loaded from the pool before the row is written there, takes the row from
+  // LDS in place of the slot's old contents, and the rows are written to the
+  // pool with the finished pieces after the wave's last chunk (a store amid
+  // the stream would hold up the loads issued after it).  Rows beyond the
+  // store's capacity are written to the pool at once instead, before any
+  // chunk of their segment is issued: a wave's memory operations on one
+  // address take effect in program order, so the segment's loads see them.
+  // Only this wave reads a segment's last chunk.
   constexpr int NB = Core::kPipeline;
   long long to_issue = hi - lo, to_consume = hi - lo;
   typename Core::Buf buf[NB];
@@ -1068,15 +1105,34 @@ void decode_balanced_kernel(DecodeParams a) {
     }
     if (++la_pos < hi) advance(la);
   };
+  // LDS of this wave: the finished-piece queue, then the row store (entries
+  // of RENTRY bytes: the row's pool offset or -1, 8 spare, the K row, the V
+  // row).
+  char* queue = reinterpret_cast<char*>(smem + ((3 * a.S + 2 + 3) & ~3)) +
+                (size_t)wave * (a.queue_bytes + a.row_bytes);
+  char* rowst = queue + a.queue_bytes;
+  constexpr int RENTRY = 16 + 2 * ROW;
+  const int r_cap = a.row_bytes / RENTRY;
+  int r_commit = 0, r_use = 0;  // rows stored, rows substituted (the same segments, in order)
+  typedef __attribute__((address_space(1))) u32x4 g_u32x4;  // global memory
   auto commit = [&](AppendSlot& sl) {
     if constexpr (APPEND) {
       if (sl.off >= 0) {
         const int blk = uniform(sl.row.blk);
-        if (blk >= 0 && blk < a.NB && lane < ROW / 16) {  // an id outside the pool writes nothing
-          const size_t d = (size_t)blk * B * rs + (size_t)sl.off + (size_t)lane * 16;
-          *reinterpret_cast<uint4*>(kpool_w + d) = sl.row.k;
-          *reinterpret_cast<uint4*>(vpool_w + d) = sl.row.v;
+        const bool valid = blk >= 0 && blk < a.NB;  // an id outside the pool writes nothing
+        const long long d = valid ? (long long)blk * B * rs + sl.off : -1;
+        if (r_commit < r_cap) {
+          char* e = rowst + r_commit * RENTRY;
+          if (lane == 0) *reinterpret_cast<long long*>(e) = d;
+          if (lane < ROW / 16) {
+            *reinterpret_cast<u32x4*>(e + 16 + lane * 16) = make_u32x4(sl.row.k);
+            *reinterpret_cast<u32x4*>(e + 16 + ROW + lane * 16) = make_u32x4(sl.row.v);
+          }
+        } else if (valid && lane < ROW / 16) {
+          *(g_u32x4*)(kpool_w + d + lane * 16) = make_u32x4(sl.row.k);
+          *(g_u32x4*)(vpool_w + d + lane * 16) = make_u32x4(sl.row.v);
         }
+        ++r_commit;
         sl.off = -1;
       }
     }
@@ -1120,7 +1176,6 @@ void decode_balanced_kernel(DecodeParams a) {
   // acknowledged, which under a full read stream takes longer than a load.
   // A record: global destinations of the rows and of the (max, sum) pairs
   // (0: none), then G * D floats, then G pairs.
-  char* queue = reinterpret_cast<char*>(smem + ((3 * a.S + 2 + 3) & ~3)) + (size_t)wave * a.queue_bytes;
   const int q_cap = a.queue_bytes / REC;  // at least one (the plan sees to it)
   int q_n = 0;
   auto flush = [&]() {
@@ -1155,11 +1210,21 @@ void decode_balanced_kernel(DecodeParams a) {
       seg_bad = false;
       first_consume = false;
     }
-    core.consume(min(kChunk - 1, cc.L - 1 - cc.j * kChunk), a.scale_log2, cur);
+    const int lim = min(kChunk - 1, cc.L - 1 - cc.j * kChunk);
+    const bool seg_end = (cc.j == cc.n - 1);
+    if constexpr (APPEND) {
+      if (seg_end) {  // row lim is the new token
+        if (r_use < r_cap) {
+          const char* e = rowst + r_use * RENTRY;
+          core.substitute(lim, cur, e + 16, e + 16 + ROW);
+        }
+        ++r_use;
+      }
+    }
+    core.consume(lim, a.scale_log2, cur);
     commit(cur.app);
     seg_bad |= curbad;
     --to_consume;
-    const bool seg_end = (cc.j == cc.n - 1);
     if (seg_end || to_consume == 0) {
       if (q_n == q_cap) flush();
       char* rec = queue + q_n * REC;
@@ -1191,6 +1256,17 @@ void decode_balanced_kernel(DecodeParams a) {
     for (int k = 0; k < NB; ++k) step(buf[k], bad[k], buf[(k + NB - 1) % NB], bad[(k + NB - 1) % NB]);
   }
   flush();
+  if constexpr (APPEND) {
+    const int nr = min(r_commit, r_cap);
+    for (int r = 0; r < nr; ++r) {
+      const char* e = rowst + r * RENTRY;
+      const long long d = *reinterpret_cast<const long long*>(e);
+      if (d >= 0 && lane < ROW / 16) {
+        *(g_u32x4*)(kpool_w + d + lane * 16) = *reinterpret_cast<const u32x4*>(e + 16 + lane * 16);
+        *(g_u32x4*)(vpool_w + d + lane * 16) = *reinterpret_cast<const u32x4*>(e + 16 + ROW + lane * 16);
+      }
+    }
+  }
 }
 
 // Stage 2 of the balanced schedule: one wave per segment (s, g), merging the
@@ -1413,8 +1489,9 @@ hipError_t launch_stage1(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.grid);
   const dim3 block(kThreads);
   if (p.schedule == kBalanced) {
-    const size_t lds = (((size_t)(3 * p.S + 2) + 3) & ~(size_t)3) * sizeof(int) + (size_t)kWavesPerWG * p.queue_bytes;
-    if (p.append)
+    const size_t lds = (((size_t)(3 * p.S + 2) + 3) & ~(size_t)3) * sizeof(int) +
+                       (size_t)kWavesPerWG * ((size_t)p.queue_bytes + (size_t)p.row_bytes);
+    if (p.append && p.fuse_rows)
       hipLaunchKernelGGL((decode_balanced_kernel<Core, true>), grid, block, lds, stream, p);
     else
       hipLaunchKernelGGL((decode_balanced_kernel<Core, false>), grid, block, lds, stream, p);

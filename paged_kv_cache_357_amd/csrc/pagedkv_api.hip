@@ -53,6 +53,13 @@ void set_grid(long long n_wg, long long group, Plan* plan) {
   plan->grid = (int)((n_wg + span - 1) / span * span);
 }
 
+// LDS left to each wave of a balanced workgroup for its queues, a multiple of 16.
+long long balanced_wave_lds(int32_t num_seqs, int32_t head_dim, int group, int32_t dtype) {
+  const long long fixed = (long long)round_up((3 * (size_t)num_seqs + 2) * 4, 16) +
+                          (long long)pkv::kWavesPerWG * pkv::balanced_stage_bytes(dtype, head_dim, group) + 256;
+  return ((pkv::kLdsBudget - fixed) / pkv::kWavesPerWG) & ~15LL;
+}
+
 int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
                int32_t max_context_len, int32_t dtype, int32_t partition_size, Plan* plan) {
   if (num_seqs < 0 || q_heads <= 0 || kv_heads <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
@@ -75,11 +82,8 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
   // Each wave keeps its finished pieces in an LDS queue and writes them out
   // at its end; the queue takes what the prefix tables and staging tiles
   // leave of the LDS budget, and must hold at least one piece.
-  const long long lds_fixed = round_up((3 * (size_t)num_seqs + 2) * 4, 16) +
-                              (long long)pkv::kWavesPerWG * pkv::balanced_stage_bytes(dtype, head_dim, group) + 256;
-  long long queue = (pkv::kLdsBudget - lds_fixed) / pkv::kWavesPerWG;
-  if (queue > pkv::kQueueMaxBytes) queue = pkv::kQueueMaxBytes;
-  queue &= ~15LL;
+  const long long wave_lds = balanced_wave_lds(num_seqs, head_dim, group, dtype);
+  long long queue = wave_lds > pkv::kQueueMaxBytes ? pkv::kQueueMaxBytes : wave_lds;
   const bool queue_fits = queue >= pkv::piece_record_bytes(group, head_dim);
   if (partition_size == 0 && max_context_len > kAutoPartition && num_seqs <= pkv::kBalancedMaxSeqs &&
       chunk_bound < (1LL << 48) && !spills && queue_fits) {
@@ -165,6 +169,10 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   p->head_group = plan.head_group;
   p->grid = plan.grid;
   p->queue_bytes = plan.queue_bytes;
+  p->row_bytes = 0;
+  p->fuse_rows = 0;
+  p->row_b = 0;
+  p->block_size = block_size;
   p->scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   return PKV_OK;
 }
@@ -215,7 +223,7 @@ int paged_kv_append_at(void* k_cache, void* v_cache, const void* k_new, const vo
   if (!k_cache || !v_cache || !k_new || !v_new || !block_tables || !positions) return PKV_ERR_NULL;
   const hipError_t e = pkv::launch_append_at(k_cache, v_cache, k_new, v_new, block_tables, positions, slot_mapping,
                                              num_seqs, max_blocks_per_seq, block_size, num_blocks, (int)row,
-                                             static_cast<hipStream_t>(stream));
+                                             (long long)max_blocks_per_seq * block_size, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -437,6 +445,16 @@ int paged_attn_decode(float* out, const void* q, const void* k_cache, const void
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+// The rows of a fused append whose stage-1 kernel does not write them:
+// position L of every sequence whose L + 1 fits the bound, as the kernels
+// would (the partitioned kernel writes its rows itself).
+static hipError_t append_rows_apart(const pkv::DecodeParams& p, hipStream_t s) {
+  if (!p.append || p.schedule != pkv::kBalanced || p.fuse_rows) return hipSuccess;
+  // L is written when 0 <= L < max_len (L + 1 attended); max_len <= MB * B
+  return pkv::launch_append_at(const_cast<void*>(p.k), const_cast<void*>(p.v), p.k_new, p.v_new, p.tables, p.lens,
+                               nullptr, p.S, p.MB, p.block_size, p.NB, p.row_b, (long long)p.max_len, s);
+}
+
 // The fused append: the same plan and checks as the decode of L + 1 tokens,
 // plus the new rows.
 static int prepare_decode_append(float* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
@@ -450,9 +468,35 @@ static int prepare_decode_append(float* out, const void* q, void* k_cache, void*
                                 partition_size, workspace, workspace_bytes, p);
   if (st != PKV_OK) return st;
   if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+  if ((long long)num_blocks * block_size > 0x7fffffffLL) return PKV_ERR_SHAPE;  // slots are int32, as for append_at
   p->k_new = k_new;
   p->v_new = v_new;
   p->append = 1;
+  p->row_b = head_dim * (dtype == PKV_DTYPE_BF16 ? 2 : 4) * kv_heads;
+  const int group = q_heads / kv_heads;
+  // The vector-ALU balanced kernels write the rows themselves (measured
+  // equal or faster than a separate launch); the matrix-core ones measured
+  // slower that way (their registers are full), so for them the rows are
+  // written by a launch of their own before stage 1, with the same result.
+  p->fuse_rows = p->schedule == pkv::kBalanced && !(dtype == PKV_DTYPE_BF16 && group >= pkv::kMfmaMinGroup);
+  if (p->fuse_rows) {
+    // The balanced kernel keeps each segment's new row in LDS until the
+    // segment's last chunk substitutes it, and writes the rows out with the
+    // finished pieces: up to a third of the wave's LDS, the rest for pieces.
+    const long long wave_lds = balanced_wave_lds(num_seqs, head_dim, group, dtype);
+    const int entry = pkv::append_row_entry_bytes(dtype, head_dim);
+    long long rows = wave_lds / 3 / entry;
+    if (rows > pkv::kAppendRowsMax) rows = pkv::kAppendRowsMax;
+    long long queue = wave_lds - rows * entry;
+    if (queue > pkv::kQueueMaxBytes) queue = pkv::kQueueMaxBytes;
+    queue &= ~15LL;
+    if (queue < pkv::piece_record_bytes(group, head_dim)) {  // no room: rows go straight to the pool
+      rows = 0;
+      queue = p->queue_bytes;
+    }
+    p->row_bytes = (int)(rows * entry);
+    p->queue_bytes = (int)queue;
+  }
   return PKV_OK;
 }
 
@@ -468,7 +512,8 @@ int paged_attn_decode_append(float* out, const void* q, void* k_cache, void* v_c
                                        max_context_len, scale, dtype, partition_size, workspace, workspace_bytes, &p);
   if (st != PKV_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads, s);
+  hipError_t e = append_rows_apart(p, s);
+  if (e == hipSuccess) e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads, s);
   if (e == hipSuccess) e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, s);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -485,8 +530,10 @@ int paged_attn_decode_append_partitions(float* out, const void* q, void* k_cache
                                        q_heads, kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                        max_context_len, scale, dtype, partition_size, workspace, workspace_bytes, &p);
   if (st != PKV_OK) return st;
-  const hipError_t e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads,
-                                                     static_cast<hipStream_t>(stream));
+  hipError_t e = append_rows_apart(p, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)
+    e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads,
+                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -55,9 +55,19 @@ constexpr __host__ __device__ int balanced_pipeline_depth(int dtype, int head_di
 }
 
 // LDS one balanced-schedule workgroup may use (prefix tables, K staging
-// tiles, finished-piece queues), and the most any wave's queue takes.
-constexpr int kLdsBudget = 64 * 1024;
+// tiles, finished-piece queues, fused-append rows): a gfx950 workgroup may
+// allocate 160 KiB, and the balanced grid holds one workgroup per CU.  The
+// most any wave's piece queue takes, and the most rows a wave keeps (larger
+// queues measured slightly slower: the plain llama-shaped step lost about
+// 0.7% with 32 KiB queues against 16 KiB).
+constexpr int kLdsBudget = 160 * 1024;
 constexpr int kQueueMaxBytes = 16 * 1024;
+constexpr int kAppendRowsMax = 24;
+// Bytes of one fused-append row kept in LDS: its pool offset (8 bytes, -1 for
+// none, then 8 spare) and the new K and V rows of one kv head.
+constexpr __host__ __device__ int append_row_entry_bytes(int dtype, int head_dim) {
+  return 16 + 2 * head_dim * (dtype == 1 ? 2 : 4);
+}
 // Bytes of one queued finished piece: a 16-byte header (global destinations
 // of the rows and of the (max, sum) pairs), group * head_dim floats, group
 // (max, sum) pairs; a multiple of 16.
@@ -97,6 +107,10 @@ struct DecodeParams {
   int32_t head_group;     // balanced: adjacent kv heads the waves of a workgroup take in lockstep (1 or 4)
   int32_t grid;           // launched workgroups (>= n_wg; the surplus exits at once)
   int32_t queue_bytes;    // balanced: LDS bytes of each wave's finished-piece queue (>= one record)
+  int32_t row_bytes;      // balanced, fused append: LDS bytes of each wave's new rows (0: stored directly)
+  int32_t fuse_rows;      // fused append: the balanced stage-1 kernel writes the new rows itself
+  int32_t row_b;          // fused append: bytes of one token's K (or V) row over all kv heads
+  int32_t block_size;
   float scale_log2;       // scale * log2(e): scores live in the base-2 domain
 };
 

@@ -37,8 +37,9 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, 
                               int num_blocks, long long block_bytes, hipStream_t stream);
 hipError_t launch_stage_blocks(void* pool_k, void* pool_v, void* stage_k, void* stage_v, const int32_t* ids, int n,
                                int num_blocks, long long block_bytes, bool gather, hipStream_t stream);
+// Positions outside [0, pos_end) are skipped (pos_end <= MB * B).
 hipError_t launch_append_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* tables, const int32_t* positions, int32_t* slots, int N, int MB, int B,
-                            int NB, int row_bytes, hipStream_t stream);
+                            int NB, int row_bytes, long long pos_end, hipStream_t stream);
 
 }  // namespace pkv

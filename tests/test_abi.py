@@ -67,10 +67,10 @@ def test_plan_and_workspace(lib):
     assert ws >= rows * (128 + 2) * 4 and ws % 256 == 0
     assert pk.plan(8, 64, 8, 128, 16, 32768, 1, partition_size=1024) == (1024, 32)
     assert pk.plan(2, 4, 4, 128, 16, 100, 1, partition_size=16) == (16, 7)
-    # finished pieces queue in LDS: a group of 16 at head_dim 128 has room for one
-    # record per wave up to about 1250 sequences, beyond that the partitioned schedule
-    assert pk.plan(1250, 64, 4, 128, 16, 2048, 1) == (0, 1024)
-    assert pk.plan(1300, 64, 4, 128, 16, 2048, 1) == (512, 4)
+    # finished pieces queue in LDS (160 KiB per workgroup on gfx950): even the largest
+    # record (group 16, head_dim 128) fits beside the tables of 2048 sequences
+    assert pk.plan(1300, 64, 4, 128, 16, 2048, 1) == (0, 1024)
+    assert pk.plan(2048, 64, 4, 128, 16, 2048, 1) == (0, 1024)
 
 
 @pytest.mark.parametrize("args,status", [

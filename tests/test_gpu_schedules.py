@@ -145,23 +145,26 @@ def test_balanced_and_partitioned_agree(pk):
     assert float(np.max(np.abs(a.astype(np.float64) - b))) <= 2 * TOL[w.dtype]
 
 
-@pytest.mark.parametrize("case", ["g16-one-record", "g1-many-segments"])
+def _queue_workload(case):
+    rng = np.random.default_rng(358777 if case.startswith("g16") else 358778)
+    if case.startswith("g16"):
+        lens = rng.integers(1, 41, size=2048)
+        lens[17] = 700
+        return make_workload("queue-g16", lens, 64, 4, 128, 16, "bf16", 358779), 17
+    lens = rng.integers(1, 25, size=2048)
+    lens[1000] = 600
+    return make_workload("queue-g1", lens, 16, 16, 128, 16, "bf16", 358780), 1000
+
+
+@pytest.mark.parametrize("case", ["g16-three-records", "g1-many-segments"])
 def test_piece_queue_flushes_mid_stream(pk, case):
     """Each wave keeps its finished pieces in an LDS queue and writes them out
-    at its end, or when the queue is full.  Group 16 at head_dim 128 leaves
-    room for one record per wave (every piece after the first flushes the
-    queue); 2048 short sequences with 16 kv heads give each wave about 32
-    pieces against a queue of 18.  Every row is compared with the
-    partitioned schedule, and a sample with the oracle."""
-    rng = np.random.default_rng(358777 if case.startswith("g16") else 358778)
-    if case == "g16-one-record":
-        lens = rng.integers(1, 41, size=600)
-        lens[17] = 700
-        w = make_workload("queue-g16", lens, 32, 2, 128, 16, "bf16", 358779)
-    else:
-        lens = rng.integers(1, 25, size=2048)
-        lens[1000] = 600
-        w = make_workload("queue-g1", lens, 16, 16, 128, 16, "bf16", 358780)
+    at its end, or when the queue is full.  Group 16 at head_dim 128 takes
+    8 KiB a record, three per wave, against about 8 pieces per wave (2048
+    sequences x 4 kv heads); 2048 short sequences with 16 kv heads give each
+    wave about 32 pieces.  Every row is compared with the partitioned
+    schedule, and a sample with the oracle."""
+    w, long_seq = _queue_workload(case)
     _assert_balanced(pk, w)
     d = to_gpu(w)
     say(f"{case}: S={w.num_seqs} G={w.group} sum L={int(w.context_lens.sum())}")
@@ -170,7 +173,33 @@ def test_piece_queue_flushes_mid_stream(pk, case):
     e = float(np.max(np.abs(out.astype(np.float64) - part)))
     say(f"{case}: max|balanced - partitioned| = {e:.3e}")
     assert np.all(np.isfinite(out)) and e <= TOL[w.dtype]
-    seqs = sorted(set(range(0, w.num_seqs, max(1, w.num_seqs // 40))) | {17 if case.startswith("g16") else 1000,
-                                                                          w.num_seqs - 1})
+    seqs = sorted(set(range(0, w.num_seqs, max(1, w.num_seqs // 40))) | {long_seq, w.num_seqs - 1})
     ref = oracle_out(w, seqs=seqs)
     assert_parity(out, ref, w, seqs=seqs, what="queued pieces")
+
+
+def test_fused_append_rows_beyond_the_row_store(pk):
+    """The fused append keeps about 21 new rows per wave in LDS; 2048 short
+    sequences with 16 kv heads end about 32 segments per wave, so the rest
+    are written to the pool before their segments are read.  Pools and
+    outputs must equal the two-launch path (append_at, then the decode of
+    L + 1) bit for bit, and a sample must match the oracle."""
+    import oracle.paged_attention as pa
+    from workloads import raw_numpy
+    w, long_seq = _queue_workload("g1-many-segments")
+    lens1 = w.context_lens + 1
+    dt = _dt(pk, w)
+    assert pk.plan(w.num_seqs, w.q_heads, w.kv_heads, w.head_dim, w.block_size, int(lens1.max()), dt)[0] == 0
+    d = to_gpu(w)
+    out = pk.decode_append(d.q, d.k, d.v, d.kn, d.vn, d.tables, d.lens, w.scale, int(lens1.max()))
+    torch.cuda.synchronize()
+    d2 = to_gpu(w)
+    pk.append_at(d2.k, d2.v, d2.kn, d2.vn, d2.tables, d2.lens)
+    out2 = gpu_decode(pk, w, d2, lens=lens1, max_len=int(lens1.max()))
+    assert torch.equal(d.k, d2.k) and torch.equal(d.v, d2.v), "pools differ from the two-launch path"
+    out = out.cpu().numpy()
+    assert np.array_equal(out.view(np.uint32), out2.view(np.uint32)), "outputs differ from the two-launch path"
+    k2, v2 = raw_numpy(d.k.cpu()), raw_numpy(d.v.cpu())
+    seqs = sorted(set(range(0, w.num_seqs, 50)) | {long_seq, w.num_seqs - 1})
+    ref = oracle_out(w, lens=lens1, seqs=seqs, k_cache=k2, v_cache=v2)
+    assert_parity(out, ref, w, seqs=seqs, what="fused rows beyond the row store")
