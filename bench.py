@@ -338,7 +338,8 @@ def main():
         # slot mapping + K/V append in a launch of its own, then the decode of L + 1
         call = pk.DecodeCall(q, kc, vc, tables, lens, w.scale, max_len, args.partition_size)
     else:
-        # the append fused into stage 1: the wave that streams position L writes it first
+        # one call: append and decode of L + 1 (stage 1 writes the rows itself on the vector-ALU
+        # kernels; the matrix-core kernels get a launch of their own first)
         call = pk.DecodeAppendCall(q, kc, vc, kn, vn, tables, pos, w.scale, max_len, args.partition_size)
     P, NP = call.plan
     balanced = P == 0  # balanced schedule: NP is the number of worker waves
