@@ -154,6 +154,90 @@ def test_forked_generation_loop(pk, B, prompts):
     say(f"forked loop B={B}: {len(streams)} streams, {n_copies} block copies, pools bit-exact")
 
 
+@pytest.mark.parametrize("Hq,Hkv,prompts", [(4, 4, [600, 37, 5]), (8, 2, [600, 80]), (8, 2, [37, 80])],
+                         ids=["vector-balanced", "matrix-balanced", "partitioned"])
+def test_forked_generation_loop_fused_append(pk, Hq, Hkv, prompts):
+    """A forked generation loop where every step is one paged_attn_decode_append
+    call: the block manager hands out the next slot (copying a shared partial
+    block first), and the call writes each stream's new token there and
+    decodes over the grown context.  The oracle keeps its own pools (rows
+    written at the reference manager's slots) and decodes them; pools stay bit
+    for bit equal and outputs within tolerance at every step.  A 600-token
+    prompt puts the call on the balanced schedule (the vector-ALU kernel
+    writes its rows itself; the matrix-core one gets a launch of its own); the
+    short prompts keep it on the partitioned one."""
+    B, D, dtype = 16, 128, "bf16"
+    rng = np.random.default_rng(7400 + Hq + sum(prompts))
+    NB, MB, steps, fanout = 256, 48, 10, 4
+    scale = np.float32(1.0 / np.sqrt(D))
+    k = normal_storage(rng, (NB, B, Hkv, D), dtype)
+    v = normal_storage(rng, (NB, B, Hkv, D), dtype)
+    kg, vg = k.cuda(), v.cuda()
+    ko, vo = raw_numpy(k).copy(), raw_numpy(v).copy()
+    native = pk.BlockManager(NB, B, MB)
+    ref = RefBlockManager(NB, B, MB)
+
+    def copies(pairs):
+        nonlocal ko, vo
+        if pairs:
+            src = torch.tensor([p[0] for p in pairs], dtype=torch.int32, device="cuda")
+            dst = torch.tensor([p[1] for p in pairs], dtype=torch.int32, device="cuda")
+            pk.copy_blocks(kg, vg, src, dst)
+            ko = oracle_copy_blocks(ko, pairs)
+            vo = oracle_copy_blocks(vo, pairs)
+
+    streams = []
+    for L in prompts:
+        a, b = native.add_sequence(), ref.add_sequence()
+        sl, cp = native.append(a, L)
+        assert (sl, cp) == ref.append(b, L)
+        kn, vn = normal_storage(rng, (L, Hkv, D), dtype), normal_storage(rng, (L, Hkv, D), dtype)
+        pk.append(kg, vg, kn.cuda(), vn.cuda(), torch.from_numpy(np.asarray(sl, dtype=np.int32)).cuda())
+        ko.reshape(NB * B, Hkv, D)[np.asarray(sl)] = raw_numpy(kn)
+        vo.reshape(NB * B, Hkv, D)[np.asarray(sl)] = raw_numpy(vn)
+        streams.append(a)
+        for _ in range(fanout - 1):
+            c = native.fork(a)
+            assert c == ref.fork(b)
+            streams.append(c)
+    dt = pk.DTYPE_BF16
+    for step in range(steps):
+        lens_before = np.array([ref.length(s) for s in streams], dtype=np.int32)
+        slots, src, dst = native.append_batch(streams)
+        want_slots, want_pairs = [], []
+        for s in streams:
+            sl, cp = ref.append(s, 1)
+            want_slots += sl
+            want_pairs += cp
+        assert list(slots) == want_slots
+        pairs = list(zip(src.tolist(), dst.tolist()))
+        assert pairs == want_pairs
+        copies(pairs)
+        tables, lens_after = native.tables(streams, MB)
+        assert np.array_equal(lens_after, lens_before + 1)
+        kn = normal_storage(rng, (len(streams), Hkv, D), dtype)
+        vn = normal_storage(rng, (len(streams), Hkv, D), dtype)
+        q = normal_storage(rng, (len(streams), Hq, D), dtype)
+        max_len = int(lens_after.max())
+        if step == 0:
+            say(f"fused loop Hq={Hq} Hkv={Hkv} prompts={prompts}: plan "
+                f"{pk.plan(len(streams), Hq, Hkv, D, B, max_len, dt)}")
+        out = pk.decode_append(q.cuda(), kg, vg, kn.cuda(), vn.cuda(), torch.from_numpy(tables).cuda(),
+                               torch.from_numpy(lens_before).cuda(), float(scale), max_len)
+        torch.cuda.synchronize()
+        ko.reshape(NB * B, Hkv, D)[np.asarray(want_slots)] = raw_numpy(kn)
+        vo.reshape(NB * B, Hkv, D)[np.asarray(want_slots)] = raw_numpy(vn)
+        assert np.array_equal(raw_numpy(kg.cpu()), ko) and np.array_equal(raw_numpy(vg.cpu()), vo), step
+        rt = np.zeros((len(streams), MB), dtype=np.int32)
+        for i, s in enumerate(streams):
+            row = ref.table(s)
+            rt[i, :len(row)] = row
+        want = pa.oracle_decode(raw_numpy(q), ko, vo, rt, lens_before + 1, scale, dtype, B)
+        err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - want)))
+        assert err <= TOL[dtype], (step, err)
+    say(f"fused loop Hq={Hq} Hkv={Hkv}: {len(streams)} streams, {steps} steps, pools bit-exact")
+
+
 @pytest.mark.parametrize("staged", [False, True])
 def test_swap_round_trip_and_decode_unchanged(pk, staged):
     """Swap a sequence's blocks out to pinned host memory and back into
