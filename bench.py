@@ -144,11 +144,16 @@ class HipEvents:
 
 
 def kernel_sha() -> str:
+    """Hash of the stage-1 kernel sources with comments and blank lines
+    dropped, so that a counter summary stays valid across comment edits."""
     import hashlib
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -13,10 +13,14 @@
 // address.  One wavefront (64 lanes) is one worker: it streams its chunks
 // with the loads of the next chunk in flight while the current one is
 // consumed, keeps the online-softmax state of the kv head's GQA group of
-// query heads in registers, and at the end of each segment piece either
-// writes the finished rows or a partial (max, sum, accumulator) record that a
-// second kernel merges with the log-sum-exp rule.  The waves of a workgroup
-// share nothing (no LDS traffic in the loop, no barrier after the prologue).
+// query heads in registers, and at the end of each segment piece produces
+// either the finished rows or a partial (max, sum, accumulator) record that a
+// second kernel merges with the log-sum-exp rule.  Pieces wait in the wave's
+// LDS queue and are written after its last chunk: stores share the in-order
+// memory counter with the loads, so one amid the stream would hold up the
+// waits for the chunks issued after it.  The waves of a workgroup share
+// nothing after the prologue (each has its own LDS tile and queue; no barrier
+// in the loop).
 //
 // Two schedules hand out the chunks:
 //   * balanced: all segments laid end to end, (s, g) in order, are cut into
@@ -50,9 +54,15 @@
 // outputs are bitwise independent of the block layout and bitwise
 // reproducible.
 //
-// Masking: rows at or beyond a piece's end inside its last chunk are either
-// loaded from the piece's last row (ValuCore) or read as zero through a
-// bounds-checked buffer resource (MfmaCore); their scores are -inf, hence
+// Fused append (paged_attn_decode_append): the lengths are those before the
+// append, L + 1 tokens are attended, and each sequence's new K/V row goes to
+// position L.  The balanced vector-ALU kernel loads the row ahead through its
+// pipeline, keeps it in LDS, substitutes it for the slot's old contents in the
+// segment's last chunk and writes it to the pool after its last chunk; the
+// partitioned kernel writes it before its first load.
+//
+// Masking: rows at or beyond a piece's end inside its last chunk read as zero
+// through a bounds-checked buffer resource; their scores are -inf, hence
 // weight exactly 0.  Running maxima start at -1e30 rather than -inf so that a
 // lane that has seen no token yet rescales by exp2(0) = 1 instead of
 // exp2(-inf + inf) = NaN.
