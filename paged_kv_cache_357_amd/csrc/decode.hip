@@ -118,47 +118,68 @@ __device__ __forceinline__ int attended_len(const DecodeParams& a, int s) {
 // Fused append of one (sequence s, kv head g) row, as the partitioned
 // schedule does it: the new K and V rows go to position p, slot
 // T[p / B] * B + p % B of the pool ("PagedAttention Paper Breakdown", section
-// 2, Address Translation Formula; K and V share the slot).  Lanes 0 ..
-// ROW/16 - 1 carry 16 bytes each.  A block id outside [0, NB) writes nothing
+// 2, Address Translation Formula; K and V share the slot).  The row is spread
+// over the wave as dwords (dword w in lane w % 64, register w / 64), so it
+// takes one or two registers a lane.  A block id outside [0, NB) writes nothing
 // (the table window check already turns the segment's rows into NaN).  The
 // unit that writes the row is the one that later streams that row's chunk,
 // and a wave's own memory operations on one address take effect in program
 // order, so its loads see the new row.  (The balanced schedule loads the
 // row ahead through its pipeline instead; see there.)
+template <int ROW>
 struct NewRow {
-  uint4 k, v;
+  static constexpr int NWORD = ROW / 4;             // dwords of a row
+  static constexpr int NW = (NWORD + 63) / 64;      // dwords a lane holds
+  uint32_t k[NW], v[NW];
   int blk;
 };
 
 template <int ROW>
-__device__ __forceinline__ NewRow load_new_row(const DecodeParams& a, int B, int s, int g, int p, int lane) {
-  NewRow r;
+__device__ __forceinline__ NewRow<ROW> load_new_row(const DecodeParams& a, int B, int s, int g, int p, int lane) {
+  NewRow<ROW> r;
   r.blk = a.tables[(size_t)s * a.MB + p / B];
-  r.k = make_uint4(0, 0, 0, 0);
-  r.v = r.k;
-  if (lane < ROW / 16) {
-    const size_t src = ((size_t)s * a.Hkv + g) * ROW + (size_t)lane * 16;
-    r.k = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
-    r.v = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src);
+  const uint32_t* kn = reinterpret_cast<const uint32_t*>(static_cast<const char*>(a.k_new) + ((size_t)s * a.Hkv + g) * ROW);
+  const uint32_t* vn = reinterpret_cast<const uint32_t*>(static_cast<const char*>(a.v_new) + ((size_t)s * a.Hkv + g) * ROW);
+#pragma unroll
+  for (int j = 0; j < NewRow<ROW>::NW; ++j) {
+    const int w = lane + 64 * j;
+    r.k[j] = w < NewRow<ROW>::NWORD ? kn[w] : 0u;
+    r.v[j] = w < NewRow<ROW>::NWORD ? vn[w] : 0u;
   }
   return r;
 }
 
+// Stores the row's dwords at byte offset `row_off` of both pools.
 template <int ROW>
-__device__ __forceinline__ void store_new_row(const DecodeParams& a, int B, const NewRow& r, int g, int p, int lane) {
-  if (r.blk < 0 || r.blk >= a.NB || lane >= ROW / 16) return;
-  const size_t dst = (((size_t)r.blk * B + (size_t)(p % B)) * a.Hkv + g) * ROW + (size_t)lane * 16;
-  *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst) = r.k;
-  *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst) = r.v;
+__device__ __forceinline__ void put_new_row(const DecodeParams& a, const NewRow<ROW>& r, size_t row_off, int lane) {
+  typedef __attribute__((address_space(1))) uint32_t g_u32;  // global memory
+  g_u32* kd = (g_u32*)(static_cast<char*>(const_cast<void*>(a.k)) + row_off);
+  g_u32* vd = (g_u32*)(static_cast<char*>(const_cast<void*>(a.v)) + row_off);
+#pragma unroll
+  for (int j = 0; j < NewRow<ROW>::NW; ++j) {
+    const int w = lane + 64 * j;
+    if (w < NewRow<ROW>::NWORD) {
+      kd[w] = r.k[j];
+      vd[w] = r.v[j];
+    }
+  }
+}
+
+template <int ROW>
+__device__ __forceinline__ void store_new_row(const DecodeParams& a, int B, const NewRow<ROW>& r, int g, int p,
+                                              int lane) {
+  if (r.blk < 0 || r.blk >= a.NB) return;
+  put_new_row<ROW>(a, r, (((size_t)r.blk * B + (size_t)(p % B)) * a.Hkv + g) * ROW, lane);
 }
 
 // What a balanced-schedule pipeline slot loads beside its chunk: the table
 // entry of the chunk issued into the slot next, and, with the fused append,
 // the new row of a segment that begins there (see the balanced kernel).
+template <int ROW>
 struct AppendSlot {
-  int nid;         // table entry of the next chunk issued into this slot
-  NewRow row;      // fused append: the new K / V row and the table entry of its block
-  long long off;   // fused append: byte offset of the row inside its block, or -1: none
+  int nid;            // table entry of the next chunk issued into this slot
+  NewRow<ROW> row;    // fused append: the new K / V row and the table entry of its block
+  long long off;      // fused append: byte offset of the row inside its block, or -1: none
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -260,7 +281,7 @@ struct ValuCore {
   struct Buf {
     u32x4 k[NI], v[NI];
     uint32_t q[G][4];
-    AppendSlot app;  // balanced schedule: table entry ahead, fused append
+    AppendSlot<ROW> app;  // balanced schedule: table entry ahead, fused append
   };
 
   int grp, seg;
@@ -514,7 +535,7 @@ struct MfmaCore {
     u32x4 k[NK];
     VRow v[4];
     bf16x8 q[KSTEPS];
-    AppendSlot app;  // balanced schedule: table entry ahead, fused append
+    AppendSlot<ROW> app;  // balanced schedule: table entry ahead, fused append
   };
 
   int gl, cl;
@@ -741,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void decode_partitioned_kernel(DecodePara
   // Fused append: the unit holding the last position writes the new token
   // before it loads any row.
   const bool appends = a.append && L - 1 < tok_end;
-  NewRow nr;
+  NewRow<ROW> nr;
   if (appends) nr = load_new_row<ROW>(a, B, s, g, L - 1, lane);
   bool bad = false;
   int wbase = 0;
@@ -1101,7 +1122,7 @@ void decode_balanced_kernel(DecodeParams a) {
   bool first_issue = true;
   Cursor la = ic;        // lookahead cursor
   long long la_pos = lo; // chunk index of la
-  auto next_entry = [&](AppendSlot& sl) {
+  auto next_entry = [&](AppendSlot<ROW>& sl) {
     sl.off = -1;
     if (la_pos >= hi) return;
     sl.nid = a.tables[(size_t)la.s * a.MB + (la.j * kChunk) / B];
@@ -1125,7 +1146,7 @@ void decode_balanced_kernel(DecodeParams a) {
   const int r_cap = a.row_bytes / RENTRY;
   int r_commit = 0, r_use = 0;  // rows stored, rows substituted (the same segments, in order)
   typedef __attribute__((address_space(1))) u32x4 g_u32x4;  // global memory
-  auto commit = [&](AppendSlot& sl) {
+  auto commit = [&](AppendSlot<ROW>& sl) {
     if constexpr (APPEND) {
       if (sl.off >= 0) {
         const int blk = uniform(sl.row.blk);
@@ -1134,13 +1155,18 @@ void decode_balanced_kernel(DecodeParams a) {
         if (r_commit < r_cap) {
           char* e = rowst + r_commit * RENTRY;
           if (lane == 0) *reinterpret_cast<long long*>(e) = d;
-          if (lane < ROW / 16) {
-            *reinterpret_cast<u32x4*>(e + 16 + lane * 16) = make_u32x4(sl.row.k);
-            *reinterpret_cast<u32x4*>(e + 16 + ROW + lane * 16) = make_u32x4(sl.row.v);
+          uint32_t* ek = reinterpret_cast<uint32_t*>(e + 16);
+          uint32_t* ev = reinterpret_cast<uint32_t*>(e + 16 + ROW);
+#pragma unroll
+          for (int j = 0; j < NewRow<ROW>::NW; ++j) {
+            const int wd = lane + 64 * j;
+            if (wd < NewRow<ROW>::NWORD) {
+              ek[wd] = sl.row.k[j];
+              ev[wd] = sl.row.v[j];
+            }
           }
-        } else if (valid && lane < ROW / 16) {
-          *(g_u32x4*)(kpool_w + d + lane * 16) = make_u32x4(sl.row.k);
-          *(g_u32x4*)(vpool_w + d + lane * 16) = make_u32x4(sl.row.v);
+        } else if (valid) {
+          put_new_row<ROW>(a, sl.row, (size_t)d, lane);
         }
         ++r_commit;
         sl.off = -1;
@@ -1271,7 +1297,7 @@ void decode_balanced_kernel(DecodeParams a) {
     for (int r = 0; r < nr; ++r) {
       const char* e = rowst + r * RENTRY;
       const long long d = *reinterpret_cast<const long long*>(e);
-      if (d >= 0 && lane < ROW / 16) {
+      if (d >= 0 && lane < ROW / 16) {  // 16 bytes a lane from LDS
         *(g_u32x4*)(kpool_w + d + lane * 16) = *reinterpret_cast<const u32x4*>(e + 16 + lane * 16);
         *(g_u32x4*)(vpool_w + d + lane * 16) = *reinterpret_cast<const u32x4*>(e + 16 + ROW + lane * 16);
       }
