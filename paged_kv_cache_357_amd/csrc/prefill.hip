@@ -34,6 +34,19 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ u32x4 make_u32x4(const uint4& t) { return u32x4{t.x, t.y, t.z, t.w}; }
 
+// Largest x over lanes l, l ^ 16, l ^ 32 and l ^ 48, without an LDS round
+// trip: with both operands x, v_permlane16_swap leaves each lane its own x
+// in one result and lane l ^ 16's in the other (rows of 16 lanes swap in
+// pairs), and v_permlane32_swap does the same for lane l ^ 32 (measured lane
+// layout on gfx950).  The maximum is exact, so the result equals the shuffle
+// form bit for bit.
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Two floats rounded to bf16 (round to nearest even), a in the low half.
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -247,8 +260,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         x[i] = (key <= lim) ? sc[k][i >> 2][i & 3] * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, x[i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_over_lane_groups(mx);
       const bool move = mx > m_run[k] + kLazy;
       if (__any(move)) {
         const float m_new = move ? mx : m_run[k];
