@@ -1,29 +1,40 @@
 """Benchmark: one decode step of paged attention on one MI355X.
 
-A step is the whole path over one batch: slot mapping for every sequence's
-new token and the K/V append into its block, the fused score / online-softmax /
-V pass over every sequence's physical blocks (stage 1), and the merge of the
-pieces of split segments (stage 2), run as one paged_attn_decode_append call:
-with the vector-ALU kernels stage 1 writes the new rows itself, with the
-matrix-core kernels the call writes them in a launch of its own first.
---two-launch runs paged_kv_append_at and then paged_attn_decode instead.  The
-workload is the Llama-7B-shaped decode batch (64 sequences, context lengths
-uniform in [128, 2048], 32 query / 32 kv heads, head_dim 128, bf16 K/V in
-16-token blocks dealt from a shuffled pool 1.25x the blocks in use).  Each
-step appends the token at position L and attends over L + 1 tokens.
+A step is the whole path over one batch: each sequence's new token is
+appended into its block (slot T[L / B] * B + L % B), and the fused score /
+online-softmax / V pass runs over every sequence's physical blocks (stage 1),
+followed by the merge of segments split between workers (stage 2); the step
+attends over L + 1 tokens.  By default the step is one
+paged_attn_decode_shared call (prepare: the new rows and the prefix each
+sequence shares with the previous one; stage 1; stage 2), which reads blocks
+that forked siblings share once; ``--call fused`` runs
+paged_attn_decode_append and ``--call two-launch`` paged_kv_append_at then
+paged_attn_decode instead.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+The default workload is the largest one that fits one GPU: copy-on-write
+parallel sampling, 128 prompts of 1024 tokens each forked into 4 siblings
+that share the 64 prompt blocks and own private tails of 0 .. 63 tokens
+(512 sequences, 40 query / 40 kv heads, head_dim 128, bf16 K/V in 16-token
+blocks).
 
-prints one JSON line: KV GB/s of the whole step (logical K+V bytes read by
-the attention, sum(L+1) * 2 * kv_heads * head_dim * 2 B, per step time), the
-roofline of the dominant kernel (stage 1, its duration from HIP events
-recorded around it on the launch stream in every fifth step of the timed
-region, created without the system-scope fence that default events add;
-each event still leaves a bubble of a few microseconds, so the other steps
-run unbracketed; its HBM
-traffic from the committed rocprofv3 counter summary when that was taken on
-the same kernel source), and the fp64 CPU oracle timed on the host's cores
-over the same workload.
+Timing (the stated protocol): W untimed warm-up steps; then the timed region
+of exactly K steps, each preceded by writing a 1 GiB buffer (beyond L2 and
+MALL, so every step starts with cold caches) and bracketed by HIP events on
+the launch stream; the step time is the median over the K steps (min and
+10th-90th percentiles reported).  After the timed region the same number of
+flushed repetitions bracket stage 1 alone, for the roofline of that kernel,
+and K steps run back to back (warm caches) for comparison.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--call shared|fused|two-launch]
+
+prints one JSON line: logical KV GB/s of the step (sum(L+1) * 2 * kv_heads *
+head_dim * 2 B per median step time; shared prompt blocks counted once per
+sibling, as each sibling's attention reads them), the unique-byte rate
+(every physical K/V row read counted once), the roofline of stage 1, the
+fp64 CPU oracle timed on the host's cores, and in ``extra`` the flushed
+steps of the other workloads, a paged-against-contiguous A/B, a plain
+streaming-read probe, the copy-on-write block copy, the CPU-GPU swap and the
+prompt pass.
 """
 from __future__ import annotations
 
@@ -41,6 +52,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, vendor figure
+FLUSH_BYTES = 1 << 30
+# Host cores one GPU of the box may use for worker pools.
+HOST_CORES_PER_GPU = 16
 
 # Prompt pass measured after the step: sequences, new tokens per sequence and
 # tokens held (the chunk continues an earlier context), Llama-7B heads.
@@ -54,43 +68,45 @@ def prefill_flops(seqs: int, chunk: int, context: int, q_heads: int, head_dim: i
     first = context - chunk
     keys = chunk * (first + 1) + chunk * (chunk - 1) // 2  # sum of p + 1 over the chunk's positions
     return 4 * head_dim * q_heads * keys * seqs
+
+
 METRIC = "paged decode attention: KV GB/s and % of MI355X HBM peak; seq-tokens/s"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_357_amd", "csrc", f) for f in ("decode.hip", "pkv_internal.h")]
+CSRC = os.path.join(ROOT, "paged_kv_cache_357_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("decode.hip", "decode_shared.hip", "decode_core.h",
+                                                  "pkv_internal.h")]
 
 WORKLOADS = {"llama7b-decode": 2, "tiny-f32": 1, "gqa-lognormal": 3, "cow-parallel-sampling": 4,
              "long-context": 5}
+STAGE1_KERNELS = ("decode_shared_kernel", "decode_balanced_kernel", "decode_partitioned_kernel")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama7b-decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--workload", default="cow-parallel-sampling", choices=sorted(WORKLOADS))
+    ap.add_argument("--call", default="shared", choices=["shared", "fused", "two-launch"],
+                    help="entry point(s) of the step")
     ap.add_argument("--deal", default="shuffled", choices=["shuffled", "identity"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--two-launch", action="store_true",
-                    help="run the append as its own launch (paged_kv_append_at), then paged_attn_decode")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = all)")
-    ap.add_argument("--probes", action="store_true", help="also time plain HBM read / copy probes")
-    ap.add_argument("--flush-reps", type=int, default=0,
-                    help="also time this many single decode launches after a 1 GiB cache flush each")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the chosen workload only (no other workloads, A/B, probes, copy, swap, prompt pass)")
+    ap.add_argument("--extra-reps", type=int, default=10, help="flushed repetitions per extra measurement")
     ap.add_argument("--cow-pairs", type=int, default=2048,
                     help="block pairs in the copy-on-write block copy timed after the step (0 = skip)")
-    ap.add_argument("--event-every", type=int, default=5,
-                    help="bracket the stage-1 launch with HIP events in every n-th timed step (each event "
-                         "leaves a bubble of a few microseconds on the stream)")
     ap.add_argument("--swap-blocks", type=int, default=512,
                     help="blocks swapped out to pinned host memory and back after the step (0 = skip)")
-    ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the prompt-pass (prefill) attention timed after the step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain copy of this size (reference kernel for byte counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of this "
                          "workload's run with --copy-probe-mib into its traffic summary under profiles/")
+    ap.add_argument("--write-traces", metavar="TRACE_DIR",
+                    help="no GPU run: summarise a rocprofv3 --kernel-trace --stats output folder of this "
+                         "workload's run into profiles/ (kernel, calls, mean / min / max duration)")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the copy probe in those runs")
     return ap.parse_args()
 
@@ -143,6 +159,12 @@ class HipEvents:
         self.ev = []
 
 
+def stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median_ms": float(np.median(a)), "min_ms": float(a.min()), "p10_ms": float(np.percentile(a, 10)),
+            "p90_ms": float(np.percentile(a, 90)), "reps": int(a.size)}
+
+
 def kernel_sha() -> str:
     """Hash of the stage-1 kernel sources with comments and blank lines
     dropped, so that a counter summary stays valid across comment edits."""
@@ -157,14 +179,14 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(PROFILES, f"decode_stage1_{workload}_traffic.txt")
+def traffic_file(workload: str, call: str) -> str:
+    return os.path.join(PROFILES, f"decode_stage1_{workload}_{call}_traffic.txt")
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, call: str):
     """HBM bytes per stage-1 launch from the committed counter summary, or
     None when it is missing or was taken on a different kernel source."""
-    path = traffic_file(workload)
+    path = traffic_file(workload, call)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -175,9 +197,26 @@ def read_traffic(workload: str):
     if kv.get("kernel_sha") != kernel_sha() or kv.get("workload") != workload:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return {"fetch": float(kv["fetch_bytes_per_launch"]), "write": float(kv["write_bytes_per_launch"]),
+                "hbm": float(kv["hbm_bytes_per_launch"])}
     except (KeyError, ValueError):
         return None
+
+
+def unique_kv_bytes(w, lens) -> int:
+    """K+V bytes of the distinct physical rows the step's attention covers:
+    every (block, offset) slot of positions < L, counted once however many
+    sequences read it."""
+    B = w.block_size
+    slots = []
+    for s in range(w.num_seqs):
+        L = int(lens[s])
+        if L <= 0:
+            continue
+        pos = np.arange(L)
+        slots.append(w.block_tables[s, pos // B].astype(np.int64) * B + pos % B)
+    n = int(np.unique(np.concatenate(slots)).size) if slots else 0
+    return n * 2 * w.kv_heads * w.head_dim * w.elt
 
 
 def _counter_rows(folder, counter):
@@ -203,9 +242,12 @@ def _per_dispatch(rows, pattern):
     for name, disp, val in rows:
         if pattern in name:
             acc[disp] = acc.get(disp, 0.0) + val
-    if not acc:
-        raise SystemExit(f"no dispatch of a kernel matching {pattern!r}")
     return list(acc.values())
+
+
+def profile_command(args, extra=""):
+    return ("python bench.py --workload {wl} --call {call} --steps 3 --warmup 1 --no-cpu-baseline --no-extras"
+            "{extra}").format(wl=args.workload, call=args.call, extra=extra)
 
 
 def write_traffic(args):
@@ -216,43 +258,85 @@ def write_traffic(args):
     fetch_dir, write_dir = args.write_traffic
     w = make_config(WORKLOADS[args.workload], values=False)
     lens = (w.context_lens + 1).astype(np.int64)
-    algo = int(lens.sum()) * 2 * w.kv_heads * w.head_dim * w.elt
+    logical = w.kv_bytes(lens)
+    unique = unique_kv_bytes(w, lens)
     copy_kib = args.copy_mib * 1024.0
     out = {}
     for tag, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(folder, counter)
         probe = _per_dispatch(rows, "probe_copy_kernel")
+        if not probe:
+            raise SystemExit(f"no probe_copy_kernel dispatch under {folder}")
         scale = copy_kib / float(np.mean(probe))
-        stage1 = [v for pat in ("decode_balanced_kernel", "decode_partitioned_kernel")
-                  for v in (_per_dispatch(rows, pat) if any(pat in r[0] for r in rows) else [])]
-        out[tag] = (float(np.mean(stage1)), scale, len(stage1))
+        kernel = next((k for k in STAGE1_KERNELS if _per_dispatch(rows, k)), None)
+        if kernel is None:
+            raise SystemExit(f"no stage-1 dispatch under {folder}")
+        stage1 = _per_dispatch(rows, kernel)
+        out[tag] = (float(np.mean(stage1)), scale, len(stage1), kernel)
     fetch_b = out["fetch"][0] * out["fetch"][1] * 1024
     write_b = out["write"][0] * out["write"][1] * 1024
-    cmd_run = ("python bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline "
-               "--copy-probe-mib {mib}").format(wl=args.workload, mib=args.copy_mib)
-    text = f"""# HBM traffic of the stage-1 decode kernel on the {w.name} step
+    cmd_run = profile_command(args, f" --copy-probe-mib {args.copy_mib}")
+    text = f"""# HBM traffic of the stage-1 decode kernel ({out['fetch'][3]}) on the {w.name} step
 # ({w.num_seqs} sequences, {w.q_heads}/{w.kv_heads} heads, head_dim {w.head_dim}, {w.dtype} KV,
-# {w.block_size}-token blocks, context L+1), MI355X, rocprofv3 counter collection in two passes:
+# {w.block_size}-token blocks, context L+1, call {args.call}), MI355X, rocprofv3 counter collection in two passes:
 #
 #   cd /tmp && export TMPDIR=/tmp && cd <repository root> &&
-#   timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- \
+#   timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- \\
 #       {cmd_run}
-#   timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- \
+#   timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- \\
 #       {cmd_run}
-#   python bench.py --workload {args.workload} --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
+#   python bench.py --workload {args.workload} --call {args.call} --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
 #
 # Scaling: each counter is multiplied by (bytes the plain copy probe moves) / (what the counter reads
 # on it): FETCH_SIZE x {out['fetch'][1]:.4f}, WRITE_SIZE x {out['write'][1]:.4f} ({args.copy_mib} MiB copy).
 # Per stage-1 launch (mean of {out['fetch'][2]} / {out['write'][2]} dispatches): FETCH_SIZE {out['fetch'][0]:.0f} KiB,
-# WRITE_SIZE {out['write'][0]:.0f} KiB.  Algorithmic bytes per launch (sum(L+1) * 2 * Hkv * D * elt): {algo}.
+# WRITE_SIZE {out['write'][0]:.0f} KiB.  Logical KV bytes per launch (sum(L+1) * 2 * Hkv * D * elt): {logical};
+# unique KV bytes (distinct physical rows): {unique}.
 workload: {args.workload}
+call: {args.call}
+kernel: {out['fetch'][3]}
 kernel_sha: {kernel_sha()}
 fetch_bytes_per_launch: {fetch_b:.0f}
 write_bytes_per_launch: {write_b:.0f}
 hbm_bytes_per_launch: {fetch_b + write_b:.0f}
-fetch_over_algorithmic: {fetch_b / algo:.4f}
+fetch_over_logical: {fetch_b / logical:.4f}
+fetch_over_unique: {fetch_b / unique:.4f}
 """
-    with open(traffic_file(args.workload), "w") as f:
+    with open(traffic_file(args.workload, args.call), "w") as f:
+        f.write(text)
+    print(text)
+
+
+def write_traces(args):
+    """Per-kernel duration summary from a rocprofv3 --kernel-trace --stats
+    output folder (its kernel_stats CSV), written under profiles/."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(args.write_traces, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {args.write_traces}")
+    rows = []
+    for p in paths:
+        with open(p, newline="") as f:
+            rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    cmd = profile_command(args)
+    lines = [f"# rocprofv3 kernel trace of the {args.workload} step (call {args.call}), MI355X",
+             "#", "#   cd /tmp && export TMPDIR=/tmp && cd <repository root> &&",
+             f"#   timeout -k 10 300 rocprofv3 --kernel-trace --stats -d gpurun_out/trace -o run "
+             f"--output-format csv -- {cmd}",
+             f"#   python bench.py --workload {args.workload} --call {args.call} --write-traces gpurun_out/trace",
+             "#", "# The run holds 1 warm-up and 3 timed steps, then the same number of stage-1 repetitions,",
+             "# each after a 1 GiB flush (fill kernel), and 3 steps back to back.", "",
+             "| kernel | calls | mean us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = re.sub(r"\(.*", "", name)[:110]
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    text = "\n".join(lines) + "\n"
+    out = os.path.join(PROFILES, f"kernel_trace_{args.workload}_{args.call}.md")
+    with open(out, "w") as f:
         f.write(text)
     print(text)
 
@@ -271,6 +355,22 @@ def _cpu_worker(seqs):
     return len(seqs)
 
 
+def host_cores():
+    """(cores the worker pool uses, cores in this process's affinity set,
+    cgroup CPU quota or None).  The pool takes the affinity set, capped by
+    the cgroup quota and by the host share of one GPU."""
+    aff = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = max(1, int(int(q) // int(period)))
+    except (OSError, ValueError):
+        pass
+    cores = min(aff, quota if quota else aff, HOST_CORES_PER_GPU)
+    return max(1, cores), aff, quota
+
+
 def cpu_baseline(w, lens, n_seqs, min_seconds=10.0):
     """The fp64 oracle over (a sample of) the same decode, sequences spread
     over a fork pool of the host's cores, one BLAS thread each; whole passes
@@ -279,7 +379,8 @@ def cpu_baseline(w, lens, n_seqs, min_seconds=10.0):
     import multiprocessing as mp
     from workloads import raw_numpy
     seqs = list(range(w.num_seqs if n_seqs <= 0 else min(n_seqs, w.num_seqs)))
-    cores = max(1, min(16, len(os.sched_getaffinity(0)), len(seqs)))
+    cores, aff, quota = host_cores()
+    cores = max(1, min(cores, len(seqs)))
     _CPU.update(q=raw_numpy(w.q), k=raw_numpy(w.k_cache), v=raw_numpy(w.v_cache), tables=w.block_tables,
                 lens=lens, scale=w.scale, dtype=w.dtype, B=w.block_size)
     # longest first, dealt round robin, so the workers finish together
@@ -302,15 +403,113 @@ def cpu_baseline(w, lens, n_seqs, min_seconds=10.0):
             "sample": f"fp64 oracle decode of sequences 0..{len(seqs) - 1} of {w.num_seqs} "
                       f"({tokens} context tokens, all {w.q_heads} q heads) at the step's lengths L+1, "
                       f"{passes} whole passes timed together",
+            "cores_in_affinity": aff, "cgroup_cpu_quota": quota, "host_cores_per_gpu": HOST_CORES_PER_GPU,
+            "blas_threads_per_worker": 1,
             "seconds": dt, "passes": passes, "seq_tokens_per_s": tokens / dt}
 
 
 # ---------------------------------------------------------------- GPU leg
 
+class Step:
+    """One decode step of a workload resident on the GPU, with its stage split:
+    pre() (launches before stage 1), stage1(), post() (stage 2)."""
+
+    def __init__(self, pk, torch, d, w, call):
+        self.pk, self.torch, self.d, self.call_name = pk, torch, d, call
+        lens_step = (w.context_lens + 1).astype(np.int32)
+        max_len = int(lens_step.max())
+        if call == "shared":
+            self.call = pk.DecodeSharedCall(d.q, d.k, d.v, d.tables, d.pos, w.scale, max_len, d.kn, d.vn)
+            self.pre, self.stage1, self.post = self.call.prepare, self.call.attend, self.call.merge
+            self.run = self.call.run
+        elif call == "fused":
+            self.call = pk.DecodeAppendCall(d.q, d.k, d.v, d.kn, d.vn, d.tables, d.pos, w.scale, max_len)
+            self.pre = lambda: None
+            self.stage1, self.post = self.call.partitions, self.call.reduce  # stage 1 holds the row write
+            self.run = lambda: (self.call.partitions(), self.call.reduce())
+        else:
+            lens = torch.from_numpy(lens_step).to(d.q.device)
+            self.call = pk.DecodeCall(d.q, d.k, d.v, d.tables, lens, w.scale, max_len)
+            self._keep = lens
+            self.pre = lambda: pk.append_at(d.k, d.v, d.kn, d.vn, d.tables, d.pos)
+            self.stage1, self.post = self.call.partitions, self.call.reduce
+            self.run = lambda: (self.pre(), self.call.partitions(), self.call.reduce())
+
+    def kernel(self):
+        if self.call_name == "shared" and getattr(self.call, "workspace", None) is not None:
+            return "decode_shared_kernel"
+        return "decode_stage1"
+
+
+def flushed_reps(n, flush, stream_ptr, before, body, after):
+    """n repetitions of before(); [event] body() [event]; after(), each after
+    writing the flush buffer; returns the bracketed times in ms."""
+    import torch
+    ev = HipEvents(2 * n, stream_ptr)
+    for i in range(n):
+        flush.fill_(1)
+        before()
+        ev.record(2 * i)
+        body()
+        ev.record(2 * i + 1)
+        after()
+    torch.cuda.synchronize()
+    ms = [ev.ms(2 * i, 2 * i + 1) for i in range(n)]
+    ev.close()
+    return ms
+
+
+def on_gpu(w, dev, seed):
+    """A workload's tensors on the device: lengths and tables from the
+    workload; q, pools and new rows as given, or (values=False workloads)
+    N(0,1) draws in the cache dtype from a seeded device generator."""
+    import torch
+    from types import SimpleNamespace
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    if w.k_cache.numel():
+        q, kc, vc, kn, vn = (t.to(dev) for t in (w.q, w.k_cache, w.v_cache, w.k_new, w.v_new))
+    else:
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        S, NB, B, H, Hq, D = w.num_seqs, w.num_blocks, w.block_size, w.kv_heads, w.q_heads, w.head_dim
+        q = torch.randn((S, Hq, D), generator=g, device=dev, dtype=torch.float32).to(dt)
+        kc = torch.randn((NB, B, H, D), generator=g, device=dev, dtype=torch.float32).to(dt)
+        vc = torch.randn((NB, B, H, D), generator=g, device=dev, dtype=torch.float32).to(dt)
+        kn = torch.randn((S, H, D), generator=g, device=dev, dtype=torch.float32).to(dt)
+        vn = torch.randn((S, H, D), generator=g, device=dev, dtype=torch.float32).to(dt)
+    return SimpleNamespace(q=q, k=kc, v=vc, kn=kn, vn=vn, tables=torch.from_numpy(w.block_tables).to(dev),
+                           pos=torch.from_numpy(w.context_lens).to(dev))
+
+
+def measure_step(pk, torch, w, d, call, reps, warmup, flush, stream_ptr):
+    """Flushed step and stage-1 statistics of one workload and call (outside
+    the timed region of the headline)."""
+    st = Step(pk, torch, d, w, call)
+    for _ in range(warmup):
+        st.run()
+    torch.cuda.synchronize()
+    step = stats(flushed_reps(reps, flush, stream_ptr, lambda: None, st.run, lambda: None))
+    s1 = stats(flushed_reps(reps, flush, stream_ptr, st.pre, st.stage1, st.post))
+    lens = (w.context_lens + 1).astype(np.int64)
+    logical = w.kv_bytes(lens)
+    unique = unique_kv_bytes(w, lens)
+    algo = unique if call == "shared" else logical
+    return {"call": call, "step": step, "stage1": s1, "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+            "step_GBps_logical": logical / (step["median_ms"] / 1e3) / 1e9,
+            "step_GBps_unique": unique / (step["median_ms"] / 1e3) / 1e9,
+            "step_pct_of_hbm_peak": 100.0 * (algo / (step["median_ms"] / 1e3) / 1e9) / HBM_PEAK_GBS,
+            "stage1_GBps": algo / (s1["median_ms"] / 1e3) / 1e9,
+            "stage1_pct_of_hbm_peak": 100.0 * (algo / (s1["median_ms"] / 1e3) / 1e9) / HBM_PEAK_GBS,
+            "algorithmic_bytes": "unique" if call == "shared" else "logical"}
+
+
 def main():
     args = parse()
     if args.write_traffic:
         write_traffic(args)
+        return
+    if args.write_traces:
+        write_traces(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (the decode shards over "
@@ -319,11 +518,13 @@ def main():
 
     from workloads import make_config
     k = WORKLOADS[args.workload]
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     w = make_config(k, deal=args.deal)
     lens_step = (w.context_lens + 1).astype(np.int32)  # attend over the appended token too
 
     cpu = None
     if not args.no_cpu_baseline:
+        print("[bench] CPU baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, lens_step, args.cpu_seqs)  # before the GPU is touched (fork pool)
 
     import torch
@@ -331,160 +532,193 @@ def main():
     pk.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, kc, vc = w.q.to(dev), w.k_cache.to(dev), w.v_cache.to(dev)
-    kn, vn = w.k_new.to(dev), w.v_new.to(dev)
-    tables = torch.from_numpy(w.block_tables).to(dev)
-    pos = torch.from_numpy(w.context_lens).to(dev)
-    lens = torch.from_numpy(lens_step).to(dev)
-    max_len = int(lens_step.max())
-    slots = torch.empty(w.num_seqs, dtype=torch.int32, device=dev)
-    two_launch = args.two_launch
-    if two_launch:
-        # slot mapping + K/V append in a launch of its own, then the decode of L + 1
-        call = pk.DecodeCall(q, kc, vc, tables, lens, w.scale, max_len, args.partition_size)
-    else:
-        # one call: append and decode of L + 1 (stage 1 writes the rows itself on the vector-ALU
-        # kernels; the matrix-core kernels get a launch of their own first)
-        call = pk.DecodeAppendCall(q, kc, vc, kn, vn, tables, pos, w.scale, max_len, args.partition_size)
-    P, NP = call.plan
-    balanced = P == 0  # balanced schedule: NP is the number of worker waves
-
+    d = on_gpu(w, dev, 0)
+    st = Step(pk, torch, d, w, args.call)
     stream_ptr = torch.cuda.current_stream(dev).cuda_stream  # the stream every entry point launches on
-
-    def step(ev=None, i=0):
-        if two_launch:
-            pk.append_at(kc, vc, kn, vn, tables, pos, slots)  # slot mapping + K/V append, one launch
-        if ev is not None:
-            ev.record(2 * i)
-        call.partitions()
-        if ev is not None:
-            ev.record(2 * i + 1)
-        call.reduce()
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    print(f"[bench] {args.workload} call {args.call}: warm-up", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
-        step()
+        st.run()
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps; in every n-th step two events bracket the
-    # stage-1 launch (an event record leaves a bubble of a few microseconds
-    # between kernels, so the other steps run back to back).
-    every = max(1, args.event_every)
-    sampled = list(range(0, args.steps, every))
-    ev = HipEvents(2 * len(sampled), stream_ptr)
+    # Timed region: exactly K steps, each after a 1 GiB flush, each bracketed
+    # by events on the launch stream.
+    ev = HipEvents(2 * args.steps, stream_ptr)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if i % every == 0:
-            step(ev, i // every)
-        else:
-            step()
+        flush.fill_(1)
+        ev.record(2 * i)
+        st.run()
+        ev.record(2 * i + 1)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-    part_ms = float(np.mean([ev.ms(2 * j, 2 * j + 1) for j in range(len(sampled))]))
+    region_s = time.perf_counter() - t0
+    step_ms = [ev.ms(2 * i, 2 * i + 1) for i in range(args.steps)]
     ev.close()
+    step = stats(step_ms)
 
-    # After the timed region: the other launches, each bracketed alone (the
-    # separate append only exists on the two-launch path; it is timed there
-    # and, for comparison, also here).
-    ev = HipEvents(4 * 10, stream_ptr)
-    for i in range(10):
-        ev.record(4 * i)
-        pk.append_at(kc, vc, kn, vn, tables, pos, slots)
-        ev.record(4 * i + 1)
-        call.partitions()
-        ev.record(4 * i + 2)
-        call.reduce()
-        ev.record(4 * i + 3)
+    # After the timed region: stage 1 alone, flushed, and warm steps.
+    s1 = stats(flushed_reps(args.steps, flush, stream_ptr, st.pre, st.stage1, st.post))
     torch.cuda.synchronize()
-    app_ms = float(np.mean([ev.ms(4 * i, 4 * i + 1) for i in range(10)]))
-    red_ms = float(np.mean([ev.ms(4 * i + 2, 4 * i + 3) for i in range(10)]))
-    ev.close()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        st.run()
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t1) * 1e3 / args.steps
 
-    kv_bytes = w.kv_bytes(lens_step)
+    logical = w.kv_bytes(lens_step)
+    unique = unique_kv_bytes(w, lens_step)
     tokens = int(lens_step.astype(np.int64).sum())
-    value = kv_bytes / (ms_step / 1e3) / 1e9
-    achieved = kv_bytes / (part_ms / 1e3) / 1e9
-    traffic = read_traffic(args.workload)
+    ms_step = step["median_ms"]
+    value = logical / (ms_step / 1e3) / 1e9
+    algo = unique if args.call == "shared" else logical
+    achieved = algo / (s1["median_ms"] / 1e3) / 1e9
+    traffic = read_traffic(args.workload, args.call)
+    kernel = st.kernel()
+    if kernel == "decode_stage1":
+        P, NP = st.call.plan if hasattr(st.call, "plan") else (None, None)
+        kernel = "decode_balanced_kernel" if P == 0 else "decode_partitioned_kernel"
 
     extra = {
-        "kv_bytes_per_step": kv_bytes,
-        "pct_of_hbm_peak_step": 100.0 * value / HBM_PEAK_GBS,
+        "timing": "median of K steps, each after writing a 1 GiB buffer, HIP events on the launch stream",
+        "step": step,
+        "stage1": {**s1, "bracket": {"shared": "stage 1 kernel alone (prepare and merge outside the events)",
+                                     "fused": "stage-1 call (with the matrix-core kernels it also writes the "
+                                              "new rows in a launch of its own)",
+                                     "two-launch": "stage 1 kernel alone"}[args.call]},
+        "timed_region_s": region_s,
+        "warm_back_to_back_ms_per_step": warm_ms,
+        "logical_kv_bytes_per_step": logical,
+        "unique_kv_bytes_per_step": unique,
+        "step_GBps_logical": value,
+        "step_GBps_unique": unique / (ms_step / 1e3) / 1e9,
+        "pct_of_hbm_peak_step_unique": 100.0 * unique / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "pct_of_hbm_peak_step_logical": 100.0 * value / HBM_PEAK_GBS,
         "seq_tokens_per_s": tokens / (ms_step / 1e3),
         "decode_tokens_per_s": w.num_seqs / (ms_step / 1e3),
-        "partition_kernel_ms": part_ms, "partition_kernel_samples": len(sampled),
-        "reduce_kernel_ms_untimed": red_ms,
-        "append_at_kernel_ms_untimed": app_ms,
-        "append": "separate launch (append_at)" if two_launch else "paged_attn_decode_append",
-        "schedule": "balanced" if balanced else "partitioned",
-        "partition_size": P, "num_partitions": NP,
+        "call": args.call,
         "kernel_sha": kernel_sha(),
     }
 
-    if args.cow_pairs > 0:
-        # Copy-on-write block copy at this workload's block shape, on buffers
-        # of its own: pair i copies block i to block n + i of both caches.
-        n = args.cow_pairs
-        shape = (2 * n, w.block_size, w.kv_heads, w.head_dim)
-        ck = torch.empty(shape, dtype=kc.dtype, device=dev)
-        cv = torch.empty(shape, dtype=kc.dtype, device=dev)
-        ck.fill_(1)
-        cv.fill_(2)
-        src = torch.arange(n, dtype=torch.int32, device=dev)
-        dst = src + n
-        for _ in range(2):
-            pk.copy_blocks(ck, cv, src, dst)
-        cev = HipEvents(2 * 10, stream_ptr)
-        for i in range(10):
-            cev.record(2 * i)
-            pk.copy_blocks(ck, cv, src, dst)
-            cev.record(2 * i + 1)
-        torch.cuda.synchronize()
-        cms = float(np.mean([cev.ms(2 * i, 2 * i + 1) for i in range(10)]))
-        cev.close()
-        block_bytes = w.block_size * w.kv_heads * w.head_dim * kc.element_size()
-        moved = 2 * n * 2 * block_bytes  # K and V blocks, each read once and written once
-        extra["copy_blocks"] = {"kernel": "copy_blocks_kernel", "pairs": n, "block_bytes": block_bytes,
-                                "bytes_moved": moved, "ms": cms, "GBps": moved / (cms / 1e3) / 1e9,
-                                "frac_of_hbm_peak": moved / (cms / 1e3) / 1e9 / HBM_PEAK_GBS}
-        del ck, cv
-
-    if args.swap_blocks > 0:
-        # Swap scattered pool blocks out to pinned host memory and back into
-        # the same blocks (the pool ends unchanged): PCIe-bound copies.
-        n = min(args.swap_blocks, w.num_blocks)
-        ids = np.random.default_rng(357200).permutation(w.num_blocks)[:n].astype(np.int32)
-        shape = (n, w.block_size, w.kv_heads, w.head_dim)
-        hk = torch.empty(shape, dtype=kc.dtype, pin_memory=True)
-        hv = torch.empty(shape, dtype=kc.dtype, pin_memory=True)
-        dt = pk.DTYPE_BF16 if kc.dtype == torch.bfloat16 else pk.DTYPE_F32
-        staging = torch.empty(pk.swap_staging_bytes(n, w.block_size, w.kv_heads, w.head_dim, dt),
-                              dtype=torch.uint8, device=dev)
-        moved = 2 * n * w.block_size * w.kv_heads * w.head_dim * kc.element_size()  # K and V
-        runs = 1 + int(np.count_nonzero(np.diff(ids) != 1))
-        extra["swap"] = {"blocks": n, "bytes_per_direction": moved}
-        for label, st in (("staged", staging), ("per_run", None)):
-            pk.swap_out(kc, vc, ids, hk, hv, staging=st)
-            pk.swap_in(kc, vc, ids, hk, hv, staging=st)
+    if not args.no_extras:
+        reps = args.extra_reps
+        # the other workloads (values drawn on the device), shared and plain calls
+        other = {}
+        for name, kk in WORKLOADS.items():
+            if kk in (1, k):
+                continue
+            print(f"[bench] extra workload {name}", file=sys.stderr, flush=True)
+            wx = make_config(kk, values=False)
+            dx = on_gpu(wx, dev, 357300 + kk)
+            other[name] = {c: measure_step(pk, torch, wx, dx, c, reps, 2, flush, stream_ptr)
+                           for c in ("shared", "fused")}
+            del dx
+        extra["workloads"] = other
+        # the headline workload through the other calls
+        extra["headline_other_calls"] = {c: measure_step(pk, torch, w, d, c, reps, 2, flush, stream_ptr)
+                                         for c in ("fused", "shared") if c != args.call}
+        # paged (shuffled blocks) against contiguous blocks, same lengths
+        ab = {}
+        for name, kk in (("llama7b-decode", 2), ("long-context", 5)):
+            print(f"[bench] identity A/B {name}", file=sys.stderr, flush=True)
+            res = {}
+            for deal in ("shuffled", "identity"):
+                wx = make_config(kk, deal=deal, values=False)
+                dx = on_gpu(wx, dev, 357400 + kk)
+                res[deal] = measure_step(pk, torch, wx, dx, "fused", reps, 2, flush, stream_ptr)["step"]["median_ms"]
+                del dx
+            ab[name] = {"shuffled_ms": res["shuffled"], "identity_ms": res["identity"],
+                        "GBps_ratio_shuffled_over_identity": res["identity"] / res["shuffled"]}
+        extra["paged_vs_contiguous"] = ab
+        # plain streaming read and copy over 4 GiB
+        import ctypes
+        plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_357_amd", "libpkv_probes.so"))
+        for fn in (plib.pkv_probe_copy, plib.pkv_probe_read, plib.pkv_probe_fill):
+            fn.restype = ctypes.c_int
+        stream = ctypes.c_void_p(stream_ptr)
+        nb = 4 << 30
+        buf = torch.empty(nb, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        dst = torch.empty(nb // 2, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        probe = {}
+        for pname, fn in (("read", lambda: plib.pkv_probe_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nb),
+                                                               ctypes.c_void_p(sink.data_ptr()), stream)),
+                          ("copy", lambda: plib.pkv_probe_copy(ctypes.c_void_p(dst.data_ptr()),
+                                                               ctypes.c_void_p(buf.data_ptr()),
+                                                               ctypes.c_size_t(nb // 2), stream))):
+            pev = HipEvents(12, stream_ptr)
+            for i in range(6):
+                pev.record(2 * i)
+                assert fn() == 0
+                pev.record(2 * i + 1)
             torch.cuda.synchronize()
-            sev = HipEvents(4 * 5, stream_ptr)
-            for i in range(5):
-                sev.record(4 * i)
-                pk.swap_out(kc, vc, ids, hk, hv, staging=st)
-                sev.record(4 * i + 1)
-                sev.record(4 * i + 2)
-                pk.swap_in(kc, vc, ids, hk, hv, staging=st)
-                sev.record(4 * i + 3)
-            torch.cuda.synchronize()
-            out_ms = float(np.median([sev.ms(4 * i, 4 * i + 1) for i in range(5)]))
-            in_ms = float(np.median([sev.ms(4 * i + 2, 4 * i + 3) for i in range(5)]))
-            sev.close()
-            extra["swap"][label] = {"copies_per_direction": 2 if st is not None else 2 * runs,
-                                    "out_ms": out_ms, "in_ms": in_ms,
-                                    "out_GBps": moved / (out_ms / 1e3) / 1e9, "in_GBps": moved / (in_ms / 1e3) / 1e9}
-        del hk, hv, staging
+            t = float(np.median([pev.ms(2 * i, 2 * i + 1) for i in range(1, 6)]))
+            pev.close()
+            probe[pname + "_GBps"] = nb / (t / 1e3) / 1e9  # read: nb read; copy: nb / 2 read + nb / 2 written
+        extra["probe"] = probe
+        extra["stage1_pct_of_probe_read"] = 100.0 * achieved / probe["read_GBps"]
+        del buf, dst
 
-    if not args.no_prefill:
+        if args.cow_pairs > 0:
+            # Copy-on-write block copy at this workload's block shape, on buffers
+            # of its own: pair i copies block i to block n + i of both caches.
+            n = args.cow_pairs
+            shape = (2 * n, w.block_size, w.kv_heads, w.head_dim)
+            ck = torch.empty(shape, dtype=d.k.dtype, device=dev)
+            cv = torch.empty(shape, dtype=d.k.dtype, device=dev)
+            ck.fill_(1)
+            cv.fill_(2)
+            src = torch.arange(n, dtype=torch.int32, device=dev)
+            dsti = src + n
+            for _ in range(2):
+                pk.copy_blocks(ck, cv, src, dsti)
+            cms = stats(flushed_reps(reps, flush, stream_ptr, lambda: None,
+                                     lambda: pk.copy_blocks(ck, cv, src, dsti), lambda: None))["median_ms"]
+            block_bytes = w.block_size * w.kv_heads * w.head_dim * d.k.element_size()
+            moved = 2 * n * 2 * block_bytes  # K and V blocks, each read once and written once
+            extra["copy_blocks"] = {"kernel": "copy_blocks_kernel", "pairs": n, "block_bytes": block_bytes,
+                                    "bytes_moved": moved, "ms": cms, "GBps": moved / (cms / 1e3) / 1e9,
+                                    "frac_of_hbm_peak": moved / (cms / 1e3) / 1e9 / HBM_PEAK_GBS}
+            del ck, cv
+
+        if args.swap_blocks > 0:
+            # Swap scattered pool blocks out to pinned host memory and back into
+            # the same blocks (the pool ends unchanged): PCIe-bound copies.
+            n = min(args.swap_blocks, w.num_blocks)
+            ids = np.random.default_rng(357200).permutation(w.num_blocks)[:n].astype(np.int32)
+            shape = (n, w.block_size, w.kv_heads, w.head_dim)
+            hk = torch.empty(shape, dtype=d.k.dtype, pin_memory=True)
+            hv = torch.empty(shape, dtype=d.k.dtype, pin_memory=True)
+            dt = pk.DTYPE_BF16 if d.k.dtype == torch.bfloat16 else pk.DTYPE_F32
+            staging = torch.empty(pk.swap_staging_bytes(n, w.block_size, w.kv_heads, w.head_dim, dt),
+                                  dtype=torch.uint8, device=dev)
+            moved = 2 * n * w.block_size * w.kv_heads * w.head_dim * d.k.element_size()  # K and V
+            runs = 1 + int(np.count_nonzero(np.diff(ids) != 1))
+            extra["swap"] = {"blocks": n, "bytes_per_direction": moved}
+            for label, stg in (("staged", staging), ("per_run", None)):
+                pk.swap_out(d.k, d.v, ids, hk, hv, staging=stg)
+                pk.swap_in(d.k, d.v, ids, hk, hv, staging=stg)
+                torch.cuda.synchronize()
+                sev = HipEvents(4 * 5, stream_ptr)
+                for i in range(5):
+                    sev.record(4 * i)
+                    pk.swap_out(d.k, d.v, ids, hk, hv, staging=stg)
+                    sev.record(4 * i + 1)
+                    sev.record(4 * i + 2)
+                    pk.swap_in(d.k, d.v, ids, hk, hv, staging=stg)
+                    sev.record(4 * i + 3)
+                torch.cuda.synchronize()
+                out_ms = float(np.median([sev.ms(4 * i, 4 * i + 1) for i in range(5)]))
+                in_ms = float(np.median([sev.ms(4 * i + 2, 4 * i + 3) for i in range(5)]))
+                sev.close()
+                extra["swap"][label] = {"copies_per_direction": 2 if stg is not None else 2 * runs,
+                                        "out_ms": out_ms, "in_ms": in_ms,
+                                        "out_GBps": moved / (out_ms / 1e3) / 1e9,
+                                        "in_GBps": moved / (in_ms / 1e3) / 1e9}
+            del hk, hv, staging
+
         from workloads import make_workload, normal_storage
         ps = PREFILL_SHAPE
         pw = make_workload("prefill-llama7b", [ps["context"]] * ps["seqs"], ps["q_heads"], ps["kv_heads"],
@@ -497,16 +731,13 @@ def main():
         pstart = torch.arange(0, ps["seqs"] + 1, dtype=torch.int32, device=dev) * ps["chunk"]
         pout = torch.empty((ps["seqs"] * ps["chunk"], ps["q_heads"], ps["head_dim"]), dtype=torch.float32,
                            device=dev)
+
+        def prefill():
+            pk.prefill(pq, pk_, pv_, ptab, plen, pstart, pw.scale, ps["chunk"], ps["context"], out=pout)
+
         for _ in range(2):
-            pk.prefill(pq, pk_, pv_, ptab, plen, pstart, pw.scale, ps["chunk"], ps["context"], out=pout)
-        pev = HipEvents(2 * 10, stream_ptr)
-        for i in range(10):
-            pev.record(2 * i)
-            pk.prefill(pq, pk_, pv_, ptab, plen, pstart, pw.scale, ps["chunk"], ps["context"], out=pout)
-            pev.record(2 * i + 1)
-        torch.cuda.synchronize()
-        pms = float(np.mean([pev.ms(2 * i, 2 * i + 1) for i in range(10)]))
-        pev.close()
+            prefill()
+        pms = stats(flushed_reps(reps, flush, stream_ptr, lambda: None, prefill, lambda: None))["median_ms"]
         flops = prefill_flops(ps["seqs"], ps["chunk"], ps["context"], ps["q_heads"], ps["head_dim"])
         tf = flops / (pms / 1e3) / 1e12
         extra["prefill"] = {"kernel": "prefill_kernel", "shape": ps, "flops": flops, "ms": pms, "TFLOPs": tf,
@@ -515,64 +746,21 @@ def main():
                             "tokens_per_s": ps["seqs"] * ps["chunk"] / (pms / 1e3)}
         del pq, pk_, pv_, pout, pw
 
-    if args.flush_reps > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        fev = HipEvents(2 * args.flush_reps, stream_ptr)
-        for i in range(args.flush_reps):
-            flush.fill_(1)
-            fev.record(2 * i)
-            call.run()
-            fev.record(2 * i + 1)
-        torch.cuda.synchronize()
-        med = float(np.median([fev.ms(2 * i, 2 * i + 1) for i in range(args.flush_reps)]))
-        fev.close()
-        extra["flushed_decode_ms_median"] = med
-        extra["flushed_decode_GBps"] = kv_bytes / (med / 1e3) / 1e9
-        del flush
-
-    if args.probes or args.copy_probe_mib:
+    if args.copy_probe_mib:
         import ctypes
         plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_357_amd", "libpkv_probes.so"))
-        for fn in (plib.pkv_probe_copy, plib.pkv_probe_read, plib.pkv_probe_fill):
-            fn.restype = ctypes.c_int
-        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        if args.copy_probe_mib:
-            nb = args.copy_probe_mib << 20
-            src = torch.empty(nb, dtype=torch.uint8, device=dev)
-            dst = torch.empty(nb, dtype=torch.uint8, device=dev)
-            src.fill_(3)
-            torch.cuda.synchronize()
-            rc = plib.pkv_probe_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
-                                     ctypes.c_size_t(nb), stream)
-            assert rc == 0
-            torch.cuda.synchronize()
-            extra["copy_probe_bytes"] = nb
-            del src, dst
-        if args.probes:
-            nb = 4 << 30
-            buf = torch.empty(nb, dtype=torch.uint8, device=dev)
-            buf.fill_(1)
-            dst = torch.empty(nb // 2, dtype=torch.uint8, device=dev)
-            sink = torch.zeros(4, dtype=torch.int32, device=dev)
-            res = {}
-            for name, fn in (("read", lambda: plib.pkv_probe_read(ctypes.c_void_p(buf.data_ptr()),
-                                                                 ctypes.c_size_t(nb),
-                                                                 ctypes.c_void_p(sink.data_ptr()), stream)),
-                             ("copy", lambda: plib.pkv_probe_copy(ctypes.c_void_p(dst.data_ptr()),
-                                                                 ctypes.c_void_p(buf.data_ptr()),
-                                                                 ctypes.c_size_t(nb // 2), stream))):
-                pev = HipEvents(12, stream_ptr)
-                for i in range(6):
-                    pev.record(2 * i)
-                    assert fn() == 0
-                    pev.record(2 * i + 1)
-                torch.cuda.synchronize()
-                t = float(np.median([pev.ms(2 * i, 2 * i + 1) for i in range(1, 6)]))
-                pev.close()
-                moved = nb if name == "read" else nb  # copy: nb/2 read + nb/2 written
-                res[name + "_GBps"] = moved / (t / 1e3) / 1e9
-            extra["probe"] = res
-            del buf, dst
+        plib.pkv_probe_copy.restype = ctypes.c_int
+        nb = args.copy_probe_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dstb = torch.empty(nb, dtype=torch.uint8, device=dev)
+        src.fill_(3)
+        torch.cuda.synchronize()
+        rc = plib.pkv_probe_copy(ctypes.c_void_p(dstb.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                 ctypes.c_size_t(nb), ctypes.c_void_p(stream_ptr))
+        assert rc == 0
+        torch.cuda.synchronize()
+        extra["copy_probe_bytes"] = nb
+        del src, dstb
 
     line = {
         "metric": METRIC,
@@ -591,12 +779,19 @@ def main():
             "workload": w.name, "num_seqs": w.num_seqs, "context_tokens_per_step": tokens,
             "q_heads": w.q_heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
             "num_blocks": w.num_blocks, "block_layout": args.deal, "kv_dtype": w.dtype, "accumulate": "fp32",
+            "value_bytes": "logical: sum(L+1) * 2 * Hkv * D * 2 B, shared prompt blocks once per sibling",
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "decode_balanced_kernel" if balanced else "decode_partitioned_kernel",
-            "algorithmic_bytes_per_launch": kv_bytes,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None if traffic is None else traffic["hbm"],
+            "kernel": kernel,
+            "algorithmic_bytes_per_launch": algo,
+            "algorithmic_bytes": "unique (each physical K/V row read once)" if args.call == "shared"
+                                 else "logical",
+            "logical_bytes_per_launch": logical,
+            "logical_GBps": logical / (s1["median_ms"] / 1e3) / 1e9,
+            "stage1_ms_median": s1["median_ms"],
+            "fetch_over_algorithmic": None if traffic is None else traffic["fetch"] / algo,
         },
         "cpu_baseline": cpu,
         "extra": extra,

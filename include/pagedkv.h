@@ -78,8 +78,9 @@ enum pkv_dtype {
  * appended to its table when L crossed a block boundary).
  *
  *   slot_mapping [num_seqs]  int32, written: T[s][p / B] * B + p % B for
- *                            p = positions[s]; -1 when p < 0 or
- *                            p >= max_blocks_per_seq * B.
+ *                            p = positions[s]; -1 when p < 0,
+ *                            p >= max_blocks_per_seq * B, or the entry
+ *                            T[s][p / B] lies outside [0, num_blocks).
  *   block_tables [num_seqs, max_blocks_per_seq] int32, read at column p / B only.
  *   positions    [num_seqs]  int32.
  * Requires num_blocks * block_size <= INT32_MAX (slots are int32).
@@ -277,8 +278,81 @@ PKV_API int paged_attn_decode_append_reduce(float* out, const void* q, void* k_c
                                             void* stream);
 
 /*
+ * paged_attn_decode_shared — paged_attn_decode (k_new = v_new = NULL) or
+ * paged_attn_decode_append (both given) that reads the blocks neighbouring
+ * sequences share once for all of them.  Forked sequences (parallel
+ * sampling, beam search) alias the physical blocks of their common prompt
+ * until a write gives one of them a private copy ("PagedAttention and vLLM
+ * Architecture: Virtual Memory for LLM Serving", section 3, Copy-on-Write for
+ * Parallel Sampling & Beam Search; "PagedAttention Paper Breakdown", section
+ * 3, Dynamic Copy-on-Write).  The outputs are those of the decode defined
+ * above for every sequence, row by row; only the reads are shared.
+ *
+ * Sharing is found on the device, every call, from the tables: sequence s
+ * shares with sequence s - 1 the leading tokens whose table entries are
+ * equal, in whole 16-token chunks, at most the shorter of their two lengths
+ * (before the append).  Runs of neighbours that each share something form
+ * groups of at most 16 / G sequences (G = q_heads / kv_heads), which share
+ * the shortest of their neighbour-to-neighbour prefixes; a group's prefix is
+ * read once and scored against all its members' query rows on the matrix
+ * cores, and each member's own tail against its rows only.  Siblings that are
+ * not neighbours in the batch are not found (their results are the same,
+ * only their shared blocks are read once per sibling).
+ *
+ *   stages     PKV_STAGES_ALL, or the bits of the stages to enqueue, in order:
+ *              PKV_STAGE_PREPARE (the new rows of the fused append; the
+ *              shares), PKV_STAGE_ATTEND (stage 1: the score / online softmax
+ *              / V pass), PKV_STAGE_MERGE (stage 2: the log-sum-exp merge of
+ *              segments split between workers, and the rows of empty and
+ *              invalid sequences).  A call that enqueues a later stage alone
+ *              must follow one that enqueued the earlier ones, on the same
+ *              stream, with the same arguments.
+ *   workspace  at least paged_attn_decode_shared_workspace_size(...) bytes.
+ *   Everything else as paged_attn_decode (k_new = NULL) or
+ *   paged_attn_decode_append (k_new given); max_context_len bounds the
+ *   attended length.
+ *
+ * Supported: as paged_attn_decode.  With bf16 caches and num_seqs <= 2048 the
+ * shared-prefix kernels run; otherwise (fp32 caches, longer batches) the call
+ * is the plain decode with the automatic partition size, its stage 1 under
+ * PKV_STAGE_ATTEND and its stage 2 under PKV_STAGE_MERGE.  Outputs are
+ * bitwise reproducible and do not depend on which physical blocks hold the
+ * tokens; siblings given equal query rows and equal tokens get bitwise equal
+ * rows.  They may differ from paged_attn_decode's in rounding (another
+ * order of the same sums), within the stated tolerances.  Errors: those of
+ * paged_attn_decode / paged_attn_decode_append; PKV_ERR_UNSUPPORTED for
+ * unknown stage bits; PKV_ERR_NULL when only one of k_new, v_new is given.
+ */
+#define PKV_STAGE_PREPARE 1
+#define PKV_STAGE_ATTEND 2
+#define PKV_STAGE_MERGE 4
+#define PKV_STAGES_ALL 7
+PKV_API int paged_attn_decode_shared(float* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                     const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                     int32_t max_context_len, float scale, int32_t dtype, int32_t stages,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode_shared_workspace_size — bytes of workspace
+ * paged_attn_decode_shared needs for these arguments (same current device as
+ * the call).  Shared-prefix kernels: partial records for W worker waves (two
+ * records of 16 rows of head_dim + 2 floats each), num_seqs ints of shares
+ * and 4 * num_seqs + 4 ints of group layout, each rounded up to 256 bytes;
+ * otherwise paged_attn_decode_workspace_size with partition_size 0.  Host
+ * only; 0 for arguments the call would reject.
+ */
+PKV_API size_t paged_attn_decode_shared_workspace_size(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
+                                                       int32_t head_dim, int32_t block_size,
+                                                       int32_t max_context_len, int32_t dtype);
+
+/*
  * paged_attn_decode_plan — the schedule a call with these arguments uses
- * (partition_size 0 = the automatic choice).  Host only; writes
+ * (partition_size 0 = the automatic choice).  The balanced schedule's worker
+ * count follows the compute units of the calling thread's current device (a
+ * whole MI355X when no device is present), so plan, workspace size and call
+ * must be made with the same current device.  Host only; writes
  * *resolved_partition_size and *num_partitions (either may be NULL):
  * (P, partitions per sequence) for the partitioned schedule, (0, worker
  * waves) for the balanced one.  Returns PKV_OK or the error the decode call

@@ -19,6 +19,13 @@ from ._lib import (  # noqa: F401
     append_at,
     decode,
     decode_append,
+    decode_shared,
+    DecodeSharedCall,
+    shared_workspace_size,
+    STAGE_PREPARE,
+    STAGE_ATTEND,
+    STAGE_MERGE,
+    STAGES_ALL,
     load_library,
     plan,
     prefill,

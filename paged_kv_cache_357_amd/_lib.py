@@ -37,6 +37,8 @@ SIGNATURES = {
     "paged_attn_decode_append": (_c_int, _DECODE_APPEND_ARGS),
     "paged_attn_decode_append_partitions": (_c_int, _DECODE_APPEND_ARGS),
     "paged_attn_decode_append_reduce": (_c_int, _DECODE_APPEND_ARGS),
+    "paged_attn_decode_shared": (_c_int, _DECODE_APPEND_ARGS),
+    "paged_attn_decode_shared_workspace_size": (_c_sz, [_c_i32] * 7),
     "paged_attn_decode_plan": (_c_int, [_c_i32] * 8 + [_i32p, _i32p]),
     "paged_attn_decode_workspace_size": (_c_sz, [_c_i32] * 8),
     "paged_status_str": (ctypes.c_char_p, [_c_int]),
@@ -484,6 +486,72 @@ def decode_append(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens,
     over the context_lens[s] + 1 tokens; returns out [S, Hq, D] fp32."""
     return DecodeAppendCall(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, scale, max_context_len,
                             partition_size, out, workspace).run()
+
+
+STAGE_PREPARE, STAGE_ATTEND, STAGE_MERGE, STAGES_ALL = 1, 2, 4, 7  # PKV_STAGE_*
+
+
+def shared_workspace_size(num_seqs, q_heads, kv_heads, head_dim, block_size, max_context_len, dtype):
+    lib = load_library()
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.paged_attn_decode_shared_workspace_size(num_seqs, q_heads, kv_heads, head_dim, block_size,
+                                                           max_context_len, dt))
+
+
+class DecodeSharedCall:
+    """A prepared paged_attn_decode_shared call: the decode (k_new = None) or
+    the fused append + decode (k_new, v_new given) that reads blocks shared by
+    neighbouring sequences once.  ``run()`` enqueues every stage;
+    ``prepare()`` / ``attend()`` / ``merge()`` one stage each, in that order."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, k_new=None,
+                 v_new=None, out=None, workspace=None):
+        S, Hq, Hkv, D, B, NB, MB = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+        self.dev = _dev(q, k_cache, v_cache, block_tables, context_lens)
+        self.lib = load_library()
+        dt = _DTYPES[q.dtype]
+        _require((k_new is None) == (v_new is None), "give both k_new and v_new, or neither")
+        if k_new is not None:
+            _require(k_new.shape == (S, Hkv, D) and v_new.shape == (S, Hkv, D), "k_new / v_new must be [S, Hkv, D]")
+            _require(k_new.dtype == v_new.dtype == k_cache.dtype, "k_new / v_new must have the cache dtype")
+            _dev(q, k_new, v_new)
+        ws = shared_workspace_size(S, Hq, Hkv, D, B, int(max_context_len), dt)
+        if out is None:
+            out = torch.empty((S, Hq, D), dtype=torch.float32, device=self.dev)
+        _require(out.shape == (S, Hq, D) and out.dtype == torch.float32, "out must be fp32 [S, Hq, D]")
+        _dev(out)
+        if workspace is None and ws:
+            workspace = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self.out, self.workspace = out, workspace
+        self._keep = (q, k_cache, v_cache, block_tables, context_lens, k_new, v_new)
+        self.args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+                     _ptr(context_lens), S, Hq, Hkv, D, B, NB, MB, int(max_context_len), float(scale), dt)
+        self.ws_args = (_ptr(workspace), 0 if workspace is None else workspace.numel())
+
+    def _call(self, stages):
+        _check("paged_attn_decode_shared",
+               self.lib.paged_attn_decode_shared(*self.args, stages, *self.ws_args, _stream(self.dev)))
+        return self.out
+
+    def run(self):
+        return self._call(STAGES_ALL)
+
+    def prepare(self):
+        return self._call(STAGE_PREPARE)
+
+    def attend(self):
+        return self._call(STAGE_ATTEND)
+
+    def merge(self):
+        return self._call(STAGE_MERGE)
+
+
+def decode_shared(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, k_new=None, v_new=None,
+                  out=None, workspace=None) -> torch.Tensor:
+    """Paged decode (or fused append + decode) reading shared prefix blocks
+    once; returns out [S, Hq, D] fp32."""
+    return DecodeSharedCall(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, k_new, v_new,
+                            out, workspace).run()
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size=0,

@@ -28,7 +28,8 @@ HOST_CXX = os.environ.get("CXX", "g++")
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden", "-I", os.path.join(ROOT, "include")]
 
 LIBS = {
-    "libpagedkv.so": ["pagedkv_api.hip", "decode.hip", "prefill.hip", "append.hip", "block_manager.cpp"],
+    "libpagedkv.so": ["pagedkv_api.hip", "decode.hip", "decode_shared.hip", "prefill.hip", "append.hip",
+                      "block_manager.cpp"],
     "libpkv_probes.so": ["bench_probes.hip"],
 }
 

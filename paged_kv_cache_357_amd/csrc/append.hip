@@ -16,17 +16,21 @@
 namespace pkv {
 namespace {
 
+// A position outside the table or a block id outside [0, NB) gives slot -1,
+// so a stray entry can never name another block's slot (the product of an id
+// and B is taken only for ids inside the pool, where it fits in int32).
 __global__ __launch_bounds__(256) void slot_mapping_kernel(int32_t* __restrict__ slots,
                                                            const int32_t* __restrict__ tables,
                                                            const int32_t* __restrict__ positions, int S, int MB,
-                                                           int B) {
+                                                           int B, int NB) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= S) return;
   const int p = positions[s];
   int slot = -1;
   if (p >= 0 && (long long)p < (long long)MB * B) {
     const int b = p / B;
-    slot = tables[(size_t)s * MB + b] * B + (p - b * B);
+    const int blk = tables[(size_t)s * MB + b];
+    if (blk >= 0 && blk < NB) slot = blk * B + (p - b * B);
   }
   slots[s] = slot;
 }
@@ -205,11 +209,11 @@ hipError_t launch_append_at(void* k_cache, void* v_cache, const void* k_new, con
 }
 
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* tables, const int32_t* positions, int S, int MB,
-                               int B, hipStream_t stream) {
+                               int B, int NB, hipStream_t stream) {
   if (S == 0) return hipSuccess;
   const int threads = 256;
   hipLaunchKernelGGL(slot_mapping_kernel, dim3((S + threads - 1) / threads), dim3(threads), 0, stream, slots,
-                     tables, positions, S, MB, B);
+                     tables, positions, S, MB, B, NB);
   return hipGetLastError();
 }
 

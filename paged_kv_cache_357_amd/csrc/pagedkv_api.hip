@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "pagedkv.h"
 #include "pkv_internal.h"
 #include "pkv_ops.h"
@@ -14,6 +16,39 @@
 namespace {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Compute units and XCDs of the calling thread's current device, queried once
+// per device.  Without a device (the planning calls used on a host with no
+// GPU) a whole MI355X is assumed: 256 CUs in 8 XCDs.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
+
+struct ChipShape {
+  int cus;
+  int xcds;
+};
+
+ChipShape chip_shape() {
+  ChipShape c{pkv::kCUsPerXcd * pkv::kMaxXcds, pkv::kMaxXcds};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();  // leave no sticky error behind for the caller
+    return c;
+  }
+  int cus = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      return c;
+    }
+    g_device_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  c.cus = cus;
+  c.xcds = cus / pkv::kCUsPerXcd;
+  if (c.xcds < 1) c.xcds = 1;
+  if (c.xcds > pkv::kMaxXcds) c.xcds = pkv::kMaxXcds;
+  return c;
+}
 
 bool valid_dtype(int dtype) { return dtype == PKV_DTYPE_F32 || dtype == PKV_DTYPE_BF16; }
 int elt_bytes(int dtype) { return dtype == PKV_DTYPE_BF16 ? 2 : 4; }
@@ -25,13 +60,17 @@ struct Plan {
   int n_units = 0;       // partitioned: decode units; balanced: worker waves
   int n_wg = 0;
   int xcd_group = 0;
+  int xcds = pkv::kMaxXcds;
   int head_group = 1;
   int grid = 0;
   int queue_bytes = 0;   // balanced: LDS queue of finished pieces per wave
   size_t acc_bytes = 0;  // workspace region of partial accumulators
   size_t ml_bytes = 0;   // workspace region of partial (max, sum) pairs
   size_t pref_bytes = 0; // workspace region of per-sequence chunk and cost prefix sums (balanced)
-  size_t total() const { return acc_bytes + ml_bytes + pref_bytes; }
+  size_t share_bytes = 0;  // shared-prefix decode: per-sequence shares with the previous sequence
+  size_t grp_bytes = 0;    // shared-prefix decode: group layout for the merge
+  bool shared = false;     // the shared-prefix kernels run this plan
+  size_t total() const { return acc_bytes + ml_bytes + pref_bytes + share_bytes + grp_bytes; }
 };
 
 // Automatic partition size of the partitioned schedule.  A batch whose
@@ -47,7 +86,7 @@ int auto_partition(int max_len) {
 
 // Consecutive logical workgroups put on one XCD, and the launched grid.
 void set_grid(long long n_wg, long long group, Plan* plan) {
-  const long long span = (long long)pkv::kXcds * group;
+  const long long span = (long long)plan->xcds * group;
   plan->n_wg = (int)n_wg;
   plan->xcd_group = (int)group;
   plan->grid = (int)((n_wg + span - 1) / span * span);
@@ -73,11 +112,15 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
       (partition_size < pkv::kChunk || partition_size > pkv::kMaxPartition || partition_size % pkv::kChunk))
     return PKV_ERR_UNSUPPORTED;
   if ((long long)num_seqs * q_heads > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  const ChipShape chip = chip_shape();
+  plan->xcds = chip.xcds;
 
   // Balanced schedule: automatic partitioning, some sequence longer than one
   // partition, a batch whose tables fit in LDS, and chunk counts whose
   // products with the worker count stay within 62 bits.
   const long long chunk_bound = (long long)num_seqs * kv_heads * ((max_context_len + pkv::kChunk - 1) / pkv::kChunk);
+  // the kernels keep chunk and cost prefix sums over sequences in int
+  const bool sums_fit = (long long)num_seqs * ((max_context_len + pkv::kChunk - 1) / pkv::kChunk + 2) < (1LL << 31);
   const bool spills = dtype == PKV_DTYPE_F32 && head_dim == 128 && group == 16;  // one wave per SIMD is not enough
   // Each wave keeps its finished pieces in an LDS queue and writes them out
   // at its end; the queue takes what the prefix tables and staging tiles
@@ -86,9 +129,9 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
   long long queue = wave_lds > pkv::kQueueMaxBytes ? pkv::kQueueMaxBytes : wave_lds;
   const bool queue_fits = queue >= pkv::piece_record_bytes(group, head_dim);
   if (partition_size == 0 && max_context_len > kAutoPartition && num_seqs <= pkv::kBalancedMaxSeqs &&
-      chunk_bound < (1LL << 48) && !spills && queue_fits) {
+      chunk_bound < (1LL << 48) && sums_fit && !spills && queue_fits) {
     const long long waves =
-        (long long)pkv::kCUs * pkv::kSimdsPerCU * pkv::balanced_waves_per_simd(dtype, head_dim, group);
+        (long long)chip.cus * pkv::kSimdsPerCU * pkv::balanced_waves_per_simd(dtype, head_dim, group);
     plan->schedule = pkv::kBalanced;
     plan->P = 0;
     plan->NP = 0;
@@ -112,7 +155,7 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
   const long long seqs_grouped = num_seqs < pkv::kSeqGroup ? (num_seqs > 0 ? num_seqs : 1) : pkv::kSeqGroup;
   long long xg = (seqs_grouped * kv_heads) / pkv::kWavesPerWG;
   if (xg < 1) xg = 1;
-  const long long span = (long long)pkv::kXcds * xg;
+  const long long span = (long long)plan->xcds * xg;
   if ((n_wg + span - 1) / span * span > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
   plan->schedule = pkv::kPartitioned;
   plan->P = P;
@@ -127,15 +170,50 @@ int plan_sizes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head
   return PKV_OK;
 }
 
-int prepare_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
-                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
-                   int32_t kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                   int32_t max_blocks_per_seq, int32_t max_context_len, float scale, int32_t dtype,
-                   int32_t partition_size, void* workspace, size_t workspace_bytes, pkv::DecodeParams* p) {
-  Plan plan;
-  int st = plan_sizes(num_seqs, q_heads, kv_heads, head_dim, block_size, max_context_len, dtype, partition_size,
-                      &plan);
+// Shared-prefix plan ("PagedAttention and vLLM Architecture", section 3:
+// forked sequences share their prompt's blocks): the balanced layout of
+// (group, kv head group) segments on matrix-core workers.  Applies to bf16
+// caches and batches whose tables fit the LDS; *applies is false (and the
+// plain plan is returned) otherwise.
+int plan_shared(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t max_context_len, int32_t dtype, Plan* plan) {
+  int st = plan_sizes(num_seqs, q_heads, kv_heads, head_dim, block_size, max_context_len, dtype, 0, plan);
   if (st != PKV_OK) return st;
+  if (dtype != PKV_DTYPE_BF16 || num_seqs < 1 || num_seqs > pkv::kBalancedMaxSeqs) return PKV_OK;
+  if ((long long)num_seqs * ((max_context_len + pkv::kChunk - 1) / pkv::kChunk + 2) >= (1LL << 31)) return PKV_OK;
+  const long long fixed = (long long)round_up((size_t)pkv::shared_lds_ints(num_seqs) * 4, 16) +
+                          (long long)pkv::kWavesPerWG * pkv::balanced_stage_bytes(dtype, head_dim, pkv::kSharedCols) +
+                          256;
+  long long queue = ((pkv::kLdsBudget - fixed) / pkv::kWavesPerWG) & ~15LL;
+  if (queue > pkv::kQueueMaxBytes) queue = pkv::kQueueMaxBytes;
+  if (queue < pkv::shared_record_bytes(pkv::kSharedCols, head_dim)) return PKV_OK;
+  const ChipShape chip = chip_shape();
+  Plan sp;
+  sp.shared = true;
+  sp.xcds = chip.xcds;
+  sp.schedule = pkv::kBalanced;
+  sp.queue_bytes = (int)queue;
+  sp.head_group = kv_heads % 4 == 0 ? 4 : 1;
+  const long long waves = (long long)chip.cus * pkv::kSimdsPerCU;  // one matrix-core worker wave per SIMD
+  sp.n_units = (int)waves;
+  set_grid(waves / pkv::kWavesPerWG, pkv::kBalancedXcdGroup, &sp);
+  const size_t rows = (size_t)waves * 2 * pkv::kSharedCols;  // two partial slots per wave, a row per column
+  sp.acc_bytes = round_up(rows * head_dim * sizeof(float), 256);
+  sp.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
+  sp.share_bytes = round_up((size_t)num_seqs * sizeof(int32_t), 256);
+  sp.grp_bytes = round_up((4 * (size_t)num_seqs + 4) * sizeof(int32_t), 256);
+  *plan = sp;
+  return PKV_OK;
+}
+
+// Checks every pointer and size of a decode call against `plan` and fills
+// the kernel parameters.
+int fill_decode(const Plan& plan, float* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                int32_t kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                int32_t max_blocks_per_seq, int32_t max_context_len, float scale, void* workspace,
+                size_t workspace_bytes, pkv::DecodeParams* p) {
+  (void)head_dim;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
   if ((long long)max_context_len > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
   if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)) return PKV_ERR_NULL;
@@ -146,6 +224,9 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   p->ws_acc = ws ? reinterpret_cast<float*>(ws) : nullptr;
   p->ws_ml = ws ? reinterpret_cast<float2*>(ws + plan.acc_bytes) : nullptr;
   p->ws_pref = ws ? reinterpret_cast<int32_t*>(ws + plan.acc_bytes + plan.ml_bytes) : nullptr;
+  p->ws_share = plan.shared ? reinterpret_cast<int32_t*>(ws + plan.acc_bytes + plan.ml_bytes + plan.pref_bytes) : nullptr;
+  p->ws_grp = plan.shared ? p->ws_share + plan.share_bytes / sizeof(int32_t) : nullptr;
+  p->max_members = plan.shared ? pkv::kSharedCols / (q_heads / kv_heads) : 0;
   p->schedule = plan.schedule;
   p->q = q;
   p->k = k_cache;
@@ -166,6 +247,7 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   p->n_units = plan.n_units;
   p->n_wg = plan.n_wg;
   p->xcd_group = plan.xcd_group;
+  p->xcds = plan.xcds;
   p->head_group = plan.head_group;
   p->grid = plan.grid;
   p->queue_bytes = plan.queue_bytes;
@@ -175,6 +257,20 @@ int prepare_decode(float* out, const void* q, const void* k_cache, const void* v
   p->block_size = block_size;
   p->scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   return PKV_OK;
+}
+
+int prepare_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                   int32_t kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                   int32_t max_blocks_per_seq, int32_t max_context_len, float scale, int32_t dtype,
+                   int32_t partition_size, void* workspace, size_t workspace_bytes, pkv::DecodeParams* p) {
+  Plan plan;
+  int st = plan_sizes(num_seqs, q_heads, kv_heads, head_dim, block_size, max_context_len, dtype, partition_size,
+                      &plan);
+  if (st != PKV_OK) return st;
+  return fill_decode(plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, q_heads, kv_heads,
+                     head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, workspace,
+                     workspace_bytes, p);
 }
 
 }  // namespace
@@ -189,7 +285,8 @@ int paged_kv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, co
   if (num_seqs == 0) return PKV_OK;
   if (!slot_mapping || !block_tables || !positions) return PKV_ERR_NULL;
   const hipError_t e = pkv::launch_slot_mapping(slot_mapping, block_tables, positions, num_seqs,
-                                                max_blocks_per_seq, block_size, static_cast<hipStream_t>(stream));
+                                                max_blocks_per_seq, block_size, num_blocks,
+                                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -550,6 +647,66 @@ int paged_attn_decode_append_reduce(float* out, const void* q, void* k_cache, vo
   if (st != PKV_OK) return st;
   const hipError_t e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int paged_attn_decode_shared(float* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                             const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, float scale, int32_t dtype, int32_t stages, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (stages & ~PKV_STAGES_ALL) return PKV_ERR_UNSUPPORTED;
+  const bool fused = k_new != nullptr || v_new != nullptr;
+  if (fused && (k_new == nullptr || v_new == nullptr)) return PKV_ERR_NULL;
+  Plan plan;
+  int st = plan_shared(num_seqs, q_heads, kv_heads, head_dim, block_size, max_context_len, dtype, &plan);
+  if (st != PKV_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int group = q_heads / kv_heads;
+  if (!plan.shared) {
+    // fp32 caches or a batch too long for the LDS tables: the plain decode
+    // (no reads shared); the attend stage holds stage 1, the merge stage 2
+    pkv::DecodeParams p;
+    st = fused ? prepare_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, num_seqs,
+                                       q_heads, kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                       max_context_len, scale, dtype, 0, workspace, workspace_bytes, &p)
+               : prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, q_heads, kv_heads,
+                                head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype, 0,
+                                workspace, workspace_bytes, &p);
+    if (st != PKV_OK) return st;
+    hipError_t e = hipSuccess;
+    if (stages & PKV_STAGE_ATTEND) {
+      e = append_rows_apart(p, s);
+      if (e == hipSuccess) e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, group, s);
+    }
+    if (e == hipSuccess && (stages & PKV_STAGE_MERGE)) e = pkv::launch_decode_reduce(p, head_dim, group, s);
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  }
+  pkv::DecodeParams p;
+  st = fill_decode(plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, q_heads, kv_heads, head_dim,
+                   block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, workspace, workspace_bytes,
+                   &p);
+  if (st != PKV_OK) return st;
+  if (fused) {
+    if ((long long)num_blocks * block_size > 0x7fffffffLL) return PKV_ERR_SHAPE;  // as for paged_kv_append_at
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.append = 1;
+    p.row_b = head_dim * 2 * kv_heads;
+  }
+  hipError_t e = hipSuccess;
+  if (stages & PKV_STAGE_PREPARE) e = pkv::launch_shared_prepare(p, s);
+  if (e == hipSuccess && (stages & PKV_STAGE_ATTEND)) e = pkv::launch_shared_stage1(p, head_dim, block_size, group, s);
+  if (e == hipSuccess && (stages & PKV_STAGE_MERGE)) e = pkv::launch_shared_merge(p, head_dim, group, s);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_attn_decode_shared_workspace_size(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t max_context_len, int32_t dtype) {
+  Plan plan;
+  if (plan_shared(num_seqs, q_heads, kv_heads, head_dim, block_size, max_context_len, dtype, &plan) != PKV_OK)
+    return 0;
+  return plan.total();
 }
 
 const char* paged_status_str(int status) {

@@ -15,12 +15,14 @@ constexpr int kChunk = 16;
 constexpr int kMaxPartition = 8192;
 // Waves per decode workgroup.  Each wave is an independent worker.
 constexpr int kWavesPerWG = 4;
-// Compute units and SIMDs of an MI355X.
-constexpr int kCUs = 256;
+// SIMDs of a CDNA compute unit.
 constexpr int kSimdsPerCU = 4;
-// Accelerator complex dies of the MI355X; consecutive workgroup ids of a
-// launch are dealt round robin over them.
-constexpr int kXcds = 8;
+// Compute units of one accelerator complex die (XCD) of gfx950, each XCD
+// with its own L2; consecutive workgroup ids of a launch are dealt round robin
+// over the XCDs.  The device's CU count is queried at run time; a whole
+// MI355X has 256 CUs in 8 XCDs, a partition of it fewer.
+constexpr int kCUsPerXcd = 32;
+constexpr int kMaxXcds = 8;
 // Sequences whose tiles the partitioned schedule keeps together on one XCD.
 constexpr int kSeqGroup = 4;
 // Longest batch the balanced schedule takes (its per-sequence tables live in
@@ -104,6 +106,7 @@ struct DecodeParams {
   int32_t n_units;        // partitioned: decode units; balanced: worker waves
   int32_t n_wg;           // workgroups holding them: ceil(n_units / kWavesPerWG)
   int32_t xcd_group;      // consecutive logical workgroups kept on one XCD (0: no remap)
+  int32_t xcds;           // XCDs of the device (launched workgroup b runs on XCD b % xcds)
   int32_t head_group;     // balanced: adjacent kv heads the waves of a workgroup take in lockstep (1 or 4)
   int32_t grid;           // launched workgroups (>= n_wg; the surplus exits at once)
   int32_t queue_bytes;    // balanced: LDS bytes of each wave's finished-piece queue (>= one record)
@@ -112,11 +115,35 @@ struct DecodeParams {
   int32_t row_b;          // fused append: bytes of one token's K (or V) row over all kv heads
   int32_t block_size;
   float scale_log2;       // scale * log2(e): scores live in the base-2 domain
+  // Shared-prefix decode (decode_shared.hip) only:
+  int32_t* ws_share;      // [S] tokens sequence s shares with sequence s - 1 (0 for s = 0), prepare stage
+  int32_t* ws_grp;        // group layout for the merge: R, gstart[S+1], gpref[S+1], gcost[S+1], gid[S]
+  int32_t max_members;    // sequences one group may hold: 16 / G (one matrix-product column per query row)
 };
+
+// Shared-prefix decode: query columns of one group (its members' query rows of
+// one kv head) in a matrix-core tile, and the LDS ints its stage-1 prologue
+// keeps per sequence (attended lengths, shares with the previous sequence,
+// group ids, group starts, prefix lengths, chunk and cost prefix sums).
+constexpr int kSharedCols = 16;
+constexpr __host__ __device__ int shared_lds_ints(int num_seqs) { return 7 * num_seqs + 4; }
+// Bytes of one queued finished piece of the shared-prefix kernel with `cols`
+// query columns: a 32-byte header, cols * head_dim floats, cols (max, sum)
+// pairs; a multiple of 16.
+constexpr __host__ __device__ int shared_record_bytes(int cols, int head_dim) {
+  return (32 + cols * (4 * head_dim + 8) + 15) & ~15;
+}
 
 // Stage 1 / stage 2 launchers (decode.hip).  Return hipSuccess or the launch error.
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int block_size,
                                     int group, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, int group, hipStream_t stream);
+
+// Shared-prefix decode launchers (decode_shared.hip): the prepare stage
+// (fused-append rows, prefix shared with the previous sequence), stage 1 and
+// the merge.  bf16 caches only.
+hipError_t launch_shared_prepare(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_shared_stage1(const DecodeParams& p, int head_dim, int block_size, int group, hipStream_t stream);
+hipError_t launch_shared_merge(const DecodeParams& p, int head_dim, int group, hipStream_t stream);
 
 }  // namespace pkv

@@ -29,8 +29,9 @@ struct PrefillParams {
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int block_size, int group, hipStream_t stream);
 
 // Slot mapping and append launchers (append.hip).
+// Positions outside the table and block ids outside [0, NB) give slot -1.
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* tables, const int32_t* positions, int S, int MB,
-                               int B, hipStream_t stream);
+                               int B, int NB, hipStream_t stream);
 hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                          const int32_t* slots, int N, long long num_slots, int row_bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int n_pairs,

@@ -71,6 +71,32 @@ def test_small_slots_append_then_decode(pk, k):
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_slot_mapping_rejects_out_of_pool_entries(pk, k):
+    """Slot mapping turns a negative position, a position past the table and
+    a table entry outside the pool (one whose product with B would wrap
+    around int32 into a valid slot, and one just past the pool) into -1; the
+    other slots equal the oracle's bit for bit."""
+    w = make_small(k)
+    B, MB = w.block_size, w.block_tables.shape[1]
+    pos = w.context_lens.astype(np.int64).copy()
+    tables = w.block_tables.copy()
+    bad = set()
+    if w.num_seqs >= 4:
+        pos[0] = -1
+        pos[1] = MB * B
+        tables[2, pos[2] // B] = (1 << 28) + 1   # (2^28 + 1) * 16 wraps to 16 in int32
+        tables[3, pos[3] // B] = w.num_blocks
+        bad = {0, 1, 2, 3}
+    tables_t = torch.from_numpy(np.ascontiguousarray(tables)).cuda()
+    pos_t = torch.from_numpy(pos.astype(np.int32)).cuda()
+    slots = pk.slot_mapping(tables_t, pos_t, w.num_blocks, B).cpu().numpy().astype(np.int64)
+    good = [s for s in range(w.num_seqs) if s not in bad]
+    want = np.full(w.num_seqs, -1, dtype=np.int64)
+    want[good] = pa.oracle_slot_mapping(w.block_tables[good], pos[good], B)
+    assert np.array_equal(slots, want)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
 def test_small_append_at_matches_oracle(pk, k):
     """The one-launch slot mapping + append: slots and pools bit for bit
     against the oracle, with positions outside the table, negative ones and a

@@ -1,0 +1,273 @@
+"""GPU parity of the shared-prefix decode (paged_attn_decode_shared): forked
+sequences whose tables share their prompt's blocks ("PagedAttention and vLLM
+Architecture", section 3) have those blocks read once for the whole group,
+and every row must still equal the fp64 oracle's decode of its own sequence
+within the stated tolerance.  Fused-append pools are compared bit for bit
+with the oracle's append.  Also: bitwise determinism, invariance under
+relabelling the pool, bitwise-equal rows for siblings with equal queries and
+tokens, the stage split, NaN rows for bad lengths and bad table entries
+confined to the rows that read them, and a needle in one member's tail that
+no other member sees.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.paged_attention as pa
+from workloads import make_config, make_small, make_workload, permute_pool, poison_unused, raw_numpy
+from gpu_common import TOL, assert_parity, oracle_out, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_357_amd as pk
+    pk.load_library()
+    return pk
+
+
+def shared(pk, w, d, lens=None, append=False, max_len=None, stages=None):
+    lens = w.context_lens if lens is None else np.asarray(lens, dtype=np.int32)
+    lens_t = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to(d.q.device)
+    if max_len is None:
+        max_len = int(max(lens.max(), 0)) + (1 if append else 0)
+    call = pk.DecodeSharedCall(d.q, d.k, d.v, d.tables, lens_t, w.scale, max(int(max_len), 1),
+                               d.kn if append else None, d.vn if append else None)
+    if stages is None:
+        call.run()
+    else:
+        for st in stages:
+            getattr(call, st)()
+    torch.cuda.synchronize()
+    return call.out.cpu().numpy()
+
+
+def forked(name, n_prompts, n_sib, prompt_len, tails, q_heads, kv_heads, head_dim, block_size, seed, **kw):
+    return make_workload(name, None, q_heads, kv_heads, head_dim, block_size, "bf16", seed,
+                         prompts=(n_prompts, n_sib, prompt_len), tails=np.asarray(tails), **kw)
+
+
+# ------------------------------------------------------------------ small
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_small_shared_decode_matches_oracle(pk, k):
+    w = make_small(k)
+    say(f"shared small config {k}: S={w.num_seqs} max L={w.max_context_len}")
+    out = shared(pk, w, to_gpu(w))
+    assert_parity(out, oracle_out(w), w, what="shared decode")
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_small_shared_fused_step(pk, k):
+    """Fused append: pools bit for bit against the oracle's append; decode of
+    L + 1 against the oracle on the appended pools."""
+    w = make_small(k)
+    d = to_gpu(w)
+    out = shared(pk, w, d, append=True)
+    k2, v2 = pa.oracle_append(raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables, w.context_lens,
+                              raw_numpy(w.k_new), raw_numpy(w.v_new), w.block_size)
+    assert np.array_equal(raw_numpy(d.k.cpu()).view(np.uint8), k2.view(np.uint8))
+    assert np.array_equal(raw_numpy(d.v.cpu()).view(np.uint8), v2.view(np.uint8))
+    ref = oracle_out(w, lens=w.context_lens + 1, k_cache=k2, v_cache=v2)
+    assert_parity(out, ref, w, what="shared fused append + decode(L+1)")
+
+
+def test_stages_equal_whole_call(pk):
+    w = make_small(4)
+    whole = shared(pk, w, to_gpu(w), append=True)
+    split = shared(pk, w, to_gpu(w), append=True, stages=("prepare", "attend", "merge"))
+    assert np.array_equal(whole.view(np.uint32), split.view(np.uint32))
+
+
+def test_siblings_bitwise_and_permutation(pk):
+    """Siblings with the same query rows and no private tokens get bitwise
+    equal rows; relabelling the pool changes no bit; the result is
+    reproducible; aliasing the prompt blocks and holding private copies of
+    them give the same result within the tolerance."""
+    w3 = make_small(4, shared_q=True, zero_tails=True)
+    n_prompts, n_sib, _ = w3.meta["prompts"]
+    o3 = shared(pk, w3, to_gpu(w3))
+    for j in range(n_prompts):
+        for s in range(1, n_sib):
+            assert np.array_equal(o3[j * n_sib].view(np.uint32), o3[j * n_sib + s].view(np.uint32))
+    assert_parity(o3, oracle_out(w3), w3, what="identical siblings")
+    w = make_small(4)
+    a = shared(pk, w, to_gpu(w))
+    again = shared(pk, w, to_gpu(w))
+    assert np.array_equal(a.view(np.uint32), again.view(np.uint32)), "not deterministic"
+    perm = np.random.default_rng(404).permutation(w.num_blocks)
+    b = shared(pk, w, to_gpu(permute_pool(w, perm)))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "depends on the physical layout"
+    # private copies of every non-first sibling's prompt blocks: nothing shared any more
+    pb = w.meta["prompt_blocks"]
+    tables = w.block_tables.astype(np.int64).copy()
+    extra, nxt = [], w.num_blocks
+    for s in range(w.num_seqs):
+        if s % n_sib:
+            for blk in range(pb):
+                extra.append(int(tables[s, blk]))
+                tables[s, blk] = nxt
+                nxt += 1
+    idx = torch.tensor(extra, dtype=torch.long)
+    w2 = make_small(4)
+    w2.k_cache = torch.cat([w.k_cache, w.k_cache.index_select(0, idx)])
+    w2.v_cache = torch.cat([w.v_cache, w.v_cache.index_select(0, idx)])
+    w2.block_tables = tables.astype(np.int32)
+    w2.num_blocks = nxt
+    c = shared(pk, w2, to_gpu(w2))
+    assert float(np.max(np.abs(a.astype(np.float64) - c))) <= TOL["bf16"]
+    assert_parity(c, oracle_out(w), w, what="private copies")
+
+
+# (prompts, siblings, prompt tokens, q heads, kv heads, head_dim, block size)
+FORKS = [(3, 4, 128, 3, 3, 128, 16),    # G = 1, kv heads not a multiple of 4: one wave per worker
+         (2, 5, 96, 8, 8, 128, 16),     # G = 1, lockstep head groups
+         (2, 3, 64, 8, 2, 128, 32),     # G = 4: four members a group
+         (2, 2, 64, 16, 2, 64, 32),     # G = 8, head_dim 64: two members a group
+         (1, 3, 32, 16, 1, 128, 16),    # G = 16: one member a group (nothing shared)
+         (1, 20, 48, 4, 4, 64, 16)]     # 20 siblings of G = 1: a run split into groups of 16 and 4
+
+
+@pytest.mark.parametrize("shape", FORKS, ids=lambda s: "-".join(map(str, s)))
+def test_forks_match_oracle(pk, shape):
+    n_pr, n_sib, pl, Hq, Hkv, D, B = shape
+    rng = np.random.default_rng(sum(shape))
+    tails = rng.integers(0, 70, size=n_pr * n_sib)
+    tails[0] = 0
+    w = forked("forks", n_pr, n_sib, pl, tails, Hq, Hkv, D, B, 362000 + sum(shape))
+    say(f"forks {shape}: S={w.num_seqs} lens={w.context_lens.tolist()[:8]}..")
+    d = to_gpu(w)
+    assert_parity(shared(pk, w, d), oracle_out(w), w, what="forked decode")
+    out = shared(pk, w, d, append=True)
+    k2, v2 = pa.oracle_append(raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables, w.context_lens,
+                              raw_numpy(w.k_new), raw_numpy(w.v_new), w.block_size)
+    assert np.array_equal(raw_numpy(d.k.cpu()).view(np.uint8), k2.view(np.uint8))
+    assert_parity(out, oracle_out(w, lens=w.context_lens + 1, k_cache=k2, v_cache=v2), w,
+                  what="forked fused append + decode(L+1)")
+
+
+def test_random_forks_sweep(pk):
+    """Seeded random batches: prompts of random lengths forked a random number
+    of times, random tails, a random group size and head shape; now and then
+    an unforked sequence between them, a zero length, and prompts whose
+    lengths are not multiples of the block size (the last prompt block shared
+    but partly filled)."""
+    rng = np.random.default_rng(36301)
+    for case in range(16):
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([64, 128]))
+        B = int(rng.choice([16, 32]))
+        n_pr = int(rng.integers(1, 5))
+        n_sib = int(rng.integers(1, 7))
+        pl = int(rng.integers(1, 5)) * B
+        tails = rng.integers(0, 90, size=n_pr * n_sib)
+        w = forked(f"sweep{case}", n_pr, n_sib, pl, tails, Hkv * G, Hkv, D, B, 36310 + case)
+        lens = w.context_lens.copy()
+        if case % 3 == 0:
+            lens[-1] = 0
+        if case % 4 == 1 and w.num_seqs > 2:
+            lens[1] = max(1, pl - int(rng.integers(1, 16)))  # shorter than the prompt: shares a partial chunk
+        say(f"sweep {case}: G={G} Hkv={Hkv} D={D} B={B} lens={lens.tolist()}")
+        out = shared(pk, w, to_gpu(w), lens=lens)
+        assert_parity(out, oracle_out(w, lens=lens), w, what=f"sweep {case}")
+
+
+def test_poison_bad_lengths_and_entries(pk):
+    """NaN-filled unowned blocks never reach an output.  A bad length makes
+    only its own rows NaN; a table entry outside the pool in a member's tail
+    makes only that member's rows NaN, and one inside the shared prompt every
+    member's rows; the other rows still match the oracle."""
+    w = poison_unused(make_small(4))
+    d = to_gpu(w)
+    out = shared(pk, w, d)
+    assert_parity(out, oracle_out(w), w, what="poisoned pool")
+    n_prompts, n_sib, _ = w.meta["prompts"]
+    pb = w.meta["prompt_blocks"]
+    lens = w.context_lens.copy()
+    tables = w.block_tables.copy()
+    lens[1] = w.max_context_len + 5                     # beyond max_context_len
+    s_tail = n_sib + 2                                  # prompt 1, sibling 2: bad tail entry
+    lens[s_tail] = max(lens[s_tail], pb * w.block_size + 1)
+    tables[s_tail, pb] = w.num_blocks + 3
+    for s in range(2 * n_sib, 3 * n_sib):               # prompt 2: bad shared entry in all siblings
+        tables[s, 1] = -7
+    w2 = make_small(4)
+    w2.k_cache, w2.v_cache, w2.block_tables = w.k_cache, w.v_cache, tables
+    d2 = to_gpu(w2)
+    out2 = shared(pk, w2, d2, lens=lens, max_len=w.max_context_len)
+    nan_rows = {1, s_tail} | set(range(2 * n_sib, 3 * n_sib))
+    for s in range(w.num_seqs):
+        assert np.all(np.isnan(out2[s])) == (s in nan_rows), s
+    good = [s for s in range(w.num_seqs) if s not in nan_rows]
+    ref = pa.oracle_decode(raw_numpy(w.q), raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables, lens,
+                           w.scale, w.dtype, w.block_size, seqs=good)
+    assert_parity(out2, ref, w, seqs=good, what="bad lengths and entries")
+
+
+def test_needle_in_one_tail(pk):
+    """A key in one member's private tail that outscores everything (score
+    gap 256): that member's rows return its V row exactly, its siblings never
+    see it; a needle in the shared prompt is returned by every sibling."""
+    n_sib, pl, B, D = 4, 64, 16, 128
+    w = forked("needle", 1, n_sib, pl, [5, 20, 37, 3], 2, 2, D, B, 36330)
+    q = torch.zeros_like(w.q)
+    q[:, :, 0] = 16.0
+    k = torch.zeros_like(w.k_cache)
+    kf = k.view(w.num_blocks * B, w.kv_heads, D)
+    pos_tail = pl + 11                                # inside sibling 2's tail
+    kf[pa.slot_of(w.block_tables[2], pos_tail, B), :, 0] = 16.0
+    w.q, w.k_cache, w.scale = q, k, 1.0
+    out = shared(pk, w, to_gpu(w))
+    vf = w.v_cache.view(w.num_blocks * B, w.kv_heads, D).float().numpy()
+    want = vf[pa.slot_of(w.block_tables[2], pos_tail, B)]
+    for h in range(w.q_heads):
+        assert np.array_equal(out[2, h], want[h])
+    assert_parity(out, oracle_out(w), w, what="tail needle")
+    for s in (0, 1, 3):
+        assert not np.allclose(out[s, 0], want[0])
+    # needle in the shared prompt: every sibling returns it
+    k2 = torch.zeros_like(w.k_cache)
+    k2.view(w.num_blocks * B, w.kv_heads, D)[pa.slot_of(w.block_tables[0], 21, B), :, 0] = 16.0
+    w.k_cache = k2
+    out2 = shared(pk, w, to_gpu(w))
+    want2 = vf[pa.slot_of(w.block_tables[0], 21, B)]
+    for s in range(n_sib):
+        for h in range(w.q_heads):
+            assert np.array_equal(out2[s, h], want2[h])
+
+
+# ------------------------------------------------------------- full size
+
+def test_full_cow_shared_fused_step(pk):
+    """The benchmark's step on the full copy-on-write workload: the new rows
+    land bit for bit at the oracle's slots with every other row (and every
+    shared prompt block) untouched, and sampled rows of the decode of L + 1
+    match the oracle; repeated calls on the same pools agree bitwise."""
+    w = make_config(4)
+    d = to_gpu(w)
+    B = w.block_size
+    say(f"full cow shared: S={w.num_seqs} sum L+1={int((w.context_lens + 1).sum())}")
+    before_k = d.k.clone()
+    out = shared(pk, w, d, append=True)
+    slots = pa.oracle_slot_mapping(w.block_tables, w.context_lens, B)
+    ib = torch.int16
+    idx = torch.from_numpy(slots).cuda()
+    mask = torch.ones(w.num_blocks * B, dtype=torch.bool, device="cuda")
+    mask[idx] = False
+    flat = d.k.view(w.num_blocks * B, -1).view(ib)
+    assert torch.equal(flat.index_select(0, idx), d.kn.reshape(len(slots), -1).view(ib))
+    assert torch.equal(flat[mask], before_k.view(w.num_blocks * B, -1).view(ib)[mask])
+    del before_k, mask
+    flat_v = d.v.view(w.num_blocks * B, -1).view(ib)
+    assert torch.equal(flat_v.index_select(0, idx), d.vn.reshape(len(slots), -1).view(ib))
+    seqs = [0, 1, 2, 3, 17, 130, 257, 510, 511]
+    k2, v2 = raw_numpy(d.k.cpu()), raw_numpy(d.v.cpu())
+    ref = oracle_out(w, lens=w.context_lens + 1, seqs=seqs, k_cache=k2, v_cache=v2)
+    assert_parity(out, ref, w, seqs=seqs, what="full shared fused step")
+    # decode again on the appended pools (no append): same lengths L + 1, same rows
+    again = shared(pk, w, d, lens=w.context_lens + 1)
+    assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
