@@ -338,8 +338,9 @@ PKV_API int paged_attn_decode_shared(float* out, const void* q, void* k_cache, v
  * paged_attn_decode_shared_workspace_size — bytes of workspace
  * paged_attn_decode_shared needs for these arguments (same current device as
  * the call).  Shared-prefix kernels: partial records for W worker waves (two
- * records of 16 rows of head_dim + 2 floats each), num_seqs ints of shares
- * and 4 * num_seqs + 4 ints of group layout, each rounded up to 256 bytes;
+ * records of 16 rows of head_dim + 2 floats each), num_seqs ints of shares,
+ * 3 * num_seqs + 4 ints of group layout and W ints of split segments, each
+ * rounded up to 256 bytes;
  * otherwise paged_attn_decode_workspace_size with partition_size 0.  Host
  * only; 0 for arguments the call would reject.
  */

@@ -61,13 +61,17 @@ __device__ __forceinline__ int shared_attended_len(const DecodeParams& a, int s)
 
 // ---------------------------------------------------------------- prepare
 
-__global__ __launch_bounds__(kThreads) void shared_prepare_kernel(DecodeParams a) {
-  const int s = (int)blockIdx.x * kWavesPerWG + (int)(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (s >= a.S) return;
+// One workgroup per sequence s: the fused-append row, the rows of a sequence
+// with nothing to attend to (zeros for L = 0, NaN for a length the launch
+// cannot cover; no later stage writes them), and the share with s - 1.
+__global__ __launch_bounds__(kThreads) void shared_prepare_kernel(DecodeParams a, int head_dim) {
+  const int s = (int)blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int B = a.block_size;
   const int L = a.lens[s];
-  if (a.append && L >= 0 && L < a.max_len) {
+  const int La = shared_attended_len(a, s);
+  if (a.append && La > 0) {
     // the new token's K and V rows (all kv heads) into slot T[L / B] * B + L % B
     const int blk = a.tables[(size_t)s * a.MB + L / B];
     if (blk >= 0 && blk < a.NB) {
@@ -76,16 +80,24 @@ __global__ __launch_bounds__(kThreads) void shared_prepare_kernel(DecodeParams a
       const uint4* vn = reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + (size_t)s * a.row_b);
       uint4* kd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst);
       uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst);
-      for (int i = lane; i < a.row_b / 16; i += 64) {
-        kd[i] = kn[i];
-        vd[i] = vn[i];
+      for (int i = tid; i < a.row_b / 16; i += kThreads) {
+        const uint4 kv = kn[i];
+        const uint4 vv = vn[i];
+        kd[i] = kv;
+        vd[i] = vv;
       }
     }
   }
+  if (La <= 0) {
+    const float fill = La == 0 ? 0.0f : __builtin_nanf("");
+    float* o = a.out + (size_t)s * a.Hq * head_dim;
+    for (int i = tid; i < a.Hq * head_dim; i += kThreads) o[i] = fill;
+  }
+  if (tid >= 64) return;
   // Leading tokens shared with sequence s - 1: equal table entries, within
   // the tokens both held before this step's append, in whole chunks.
   int sh = 0;
-  if (s > 0 && shared_attended_len(a, s) >= 0 && shared_attended_len(a, s - 1) >= 0) {
+  if (s > 0 && La >= 0 && shared_attended_len(a, s - 1) >= 0) {
     const int m = min(L, a.lens[s - 1]);
     const int nb = (m + B - 1) / B;
     const int32_t* t0 = a.tables + (size_t)(s - 1) * a.MB;
@@ -260,14 +272,12 @@ void decode_shared_kernel(DecodeParams a) {
     int* gs = a.ws_grp + 1;
     int* gp = gs + S + 1;
     int* gc = gp + S + 1;
-    int* gi = gc + S + 1;
     if (tid == 0) a.ws_grp[0] = R;
     for (int i = tid; i <= R; i += kThreads) {
       gs[i] = gstart[i];
       gp[i] = gpref[i];
       gc[i] = gcost[i];
     }
-    for (int s = tid; s < S; s += kThreads) gi[s] = gidv[s];
   }
 
   // ---- this worker's share (see the balanced schedule of decode.hip)
@@ -480,6 +490,7 @@ void decode_shared_kernel(DecodeParams a) {
   bool started = false;
   bool col_bad = false;
   bool first_consume = true;
+  int split = -1;  // the segment this worker began and left to later workers
   const float nan = __builtin_nanf("");
   auto step = [&](typename Core::Buf& cur, bool curbad, typename Core::Buf& nxt, bool& nxtbad) {
     issue_next(nxt, nxtbad);
@@ -536,6 +547,7 @@ void decode_shared_kernel(DecodeParams a) {
         }
       }
       q_used += rb;
+      if (to_consume == 0 && started && !seg_end) split = cc.r * NGR + cc.g;
     }
     if (to_consume > 0) advance(cc);
   };
@@ -547,127 +559,90 @@ void decode_shared_kernel(DecodeParams a) {
     for (int k = 0; k < NB; ++k) step(buf[k], bad[k], buf[(k + NB - 1) % NB], bad[(k + NB - 1) % NB]);
   }
   flush();
+  if (hsub == 0 && lane == 0) a.ws_split[worker] = split;
 }
 
 // ------------------------------------------------------------------ merge
 
-// One wave per (sequence s, kv head g): the G query-head rows of s at kv head
-// g, which are columns k * G .. k * G + G - 1 of its group's segment (k: s's
-// index in the group).  An invalid length gives NaN rows, L = 0 zeros; a
-// segment one worker finished was written by stage 1; otherwise the pieces of
-// workers w0 .. w1 are merged in worker order, exactly as the balanced merge
-// of decode.hip does.
+// One workgroup per worker w: if w began a segment (group r, head group gg)
+// that later workers continued, the pieces of workers w .. w1 are merged into
+// the segment's rows (every column of its HG kv heads), in worker order:
+// M the largest piece max, rows sum(exp2(m_p - M) acc_p) / sum(exp2(m_p - M)
+// l_p).  A segment one worker finished was written by stage 1; the rows of
+// empty and invalid sequences by the prepare stage.  A workspace that does
+// not hold this call's stage-1 layout (no stage 1 before the merge) makes
+// the kernel write nothing rather than read out of place.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_reduce_shared_kernel(DecodeParams a) {
   constexpr int CPL = D / 64;  // columns per lane (1 or 2)
-  constexpr int KB = G <= 1 ? 8 : (G <= 2 ? 4 : (G <= 4 ? 2 : 1));
   const int lane = threadIdx.x & 63;
-  const int seg = (int)blockIdx.x * kWavesPerWG + uniform(threadIdx.x >> 6);
-  if (seg >= a.S * a.Hkv) return;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int w0 = (int)blockIdx.x;
   const int S = a.S;
-  const int s = seg / a.Hkv;
-  const int g = seg - s * a.Hkv;
-  const int L = shared_attended_len(a, s);
+  const int HG = a.head_group;
+  const int NGR = a.Hkv / HG;
   const int* gs = a.ws_grp + 1;
   const int* gp = gs + S + 1;
   const int* gc = gp + S + 1;
-  const int* gi = gc + S + 1;
-  float* o0 = a.out + ((size_t)s * a.Hq + (size_t)g * G) * D + lane * CPL;
-  if (L <= 0) {
-    const float fill = L == 0 ? 0.0f : __builtin_nanf("");
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) o0[(size_t)h * D + j] = fill;
-    return;
-  }
-  // The layout stage 1 left in the workspace; anything inconsistent (no
-  // stage 1 before this merge) gives NaN rows rather than stray reads.
   const int R = a.ws_grp[0];
-  const int r = (R >= 1 && R <= S) ? gi[s] : -1;
-  const int k = (r >= 0 && r < R) ? s - gs[r] : -1;
-  const int n = (k >= 0 && k < kSharedCols / G) ? gp[r + 1] - gp[r] : 0;
-  const int HG = a.head_group;
-  const int NGR = a.Hkv / HG;
-  const long long T = (long long)NGR * (n > 0 ? gp[R] : 1);
+  if (R < 1 || R > S) return;
+  const long long T = (long long)NGR * gp[R];
+  const long long TC = (long long)NGR * gc[R];
+  if (T <= 0 || TC <= 0) return;
   const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
-  const long long TC = (long long)NGR * (n > 0 ? gc[R] : 1);
-  const long long cbase = (long long)NGR * gc[r < 0 ? 0 : r] + (long long)(g / HG) * (n + kSegCost) + kSegCost;
-  const long long w0 = balanced_wave_of(cbase, TC, W_eff);
+  if (w0 >= W_eff) return;
+  const int split = a.ws_split[w0];
+  if (split < 0) return;
+  const int r = split / NGR;
+  const int gg = split - r * NGR;
+  const int a0 = r < R ? gs[r] : 0;
+  const int nm = r < R ? gs[r + 1] - a0 : 0;
+  const int n = r < R ? gp[r + 1] - gp[r] : 0;
+  const long long cbase = (long long)NGR * (r < R ? gc[r] : 0) + (long long)gg * (n + kSegCost) + kSegCost;
   const long long w1 = balanced_wave_of(cbase + n - 1, TC, W_eff);
-  const int hsub = g % HG;
-  if (n <= 0 || T <= 0 || TC <= 0 || cbase < 0 || cbase + n > TC || w0 < 0 || w1 >= W_eff || w0 > w1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) o0[(size_t)h * D + j] = __builtin_nanf("");
-    return;
-  }
-  if (w0 == w1) return;
+  const bool ok = r < R && nm >= 1 && nm * G <= kSharedCols && n > 0 && balanced_wave_of(cbase, TC, W_eff) == w0 &&
+                  w1 > w0 && w1 < W_eff;
+  if (!ok) return;
   const int pieces = (int)(w1 - w0 + 1);
-  auto piece_row = [&](int p) -> size_t {  // row of head 0 of s's columns; head h is + h
-    const size_t wave_id = HG == 1 ? (size_t)(w0 + p) : (size_t)(w0 + p) * kWavesPerWG + hsub;
-    return (wave_id * 2 + (p == 0 ? 1 : 0)) * kSharedCols + (size_t)k * G;
-  };
-
-  float M[G], num[G][CPL], den[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    M[h] = kNegBig;
-    den[h] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) num[h][j] = 0.0f;
-  }
-  for (int p0 = 0; p0 < pieces; p0 += KB) {
-    float2 t[KB][G];
-    float x[KB][G][CPL];
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const bool in = p0 + i < pieces;
-      const size_t rr = piece_row(in ? p0 + i : p0);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        t[i][h] = in ? a.ws_ml[rr + h] : make_float2(kNegBig, 0.0f);
-        if constexpr (CPL == 2) {
-          const float2 v = in ? *reinterpret_cast<const float2*>(a.ws_acc + (rr + h) * D + lane * CPL)
-                              : make_float2(0.0f, 0.0f);
-          x[i][h][0] = v.x;
-          x[i][h][1] = v.y;
-        } else {
-          x[i][h][0] = in ? a.ws_acc[(rr + h) * D + lane] : 0.0f;
-        }
-      }
+  const int ncols = nm * G;
+  // rows: (head of the group hsub, column c), taken by the waves in turn
+  for (int row = wave; row < HG * ncols; row += kWavesPerWG) {
+    const int hsub = row / ncols;
+    const int c = row - hsub * ncols;
+    const int s = a0 + c / G;
+    const int kvh = gg * HG + hsub;
+    auto piece_row = [&](int p) -> size_t {
+      const size_t wave_id = HG == 1 ? (size_t)(w0 + p) : (size_t)(w0 + p) * kWavesPerWG + hsub;
+      return (wave_id * 2 + (p == 0 ? 1 : 0)) * kSharedCols + (size_t)c;
+    };
+    float M = kNegBig;
+    for (int p0 = 0; p0 < pieces; p0 += 64) {
+      const int p = p0 + lane;
+      if (p < pieces) M = fmaxf(M, a.ws_ml[piece_row(p)].x);
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float Mn = M[h];
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float num[CPL], den = 0.0f;
 #pragma unroll
-      for (int i = 0; i < KB; ++i) Mn = fmaxf(Mn, t[i][h].x);
-      if (p0 > 0) {
-        const float sc = fast_exp2(M[h] - Mn);
-        den[h] *= sc;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) num[h][j] *= sc;
-      }
-      M[h] = Mn;
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        if (p0 + i < pieces) {
-          const float f = fast_exp2(t[i][h].x - M[h]);
-          den[h] = fmaf(t[i][h].y, f, den[h]);
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) num[h][j] = fmaf(x[i][h][j], f, num[h][j]);
-        }
+    for (int j = 0; j < CPL; ++j) num[j] = 0.0f;
+    for (int p = 0; p < pieces; ++p) {
+      const size_t rr = piece_row(p);
+      const float2 t = a.ws_ml[rr];
+      const float f = fast_exp2(t.x - M);
+      den = fmaf(t.y, f, den);
+      if constexpr (CPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(a.ws_acc + rr * D + lane * CPL);
+        num[0] = fmaf(v.x, f, num[0]);
+        num[1] = fmaf(v.y, f, num[1]);
+      } else {
+        num[0] = fmaf(a.ws_acc[rr * D + lane], f, num[0]);
       }
     }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float* o = o0 + (size_t)h * D;
+    float* o = a.out + ((size_t)s * a.Hq + (size_t)kvh * G + (size_t)(c % G)) * D + lane * CPL;
     if constexpr (CPL == 2) {
-      *reinterpret_cast<float2*>(o) = make_float2(num[h][0] / den[h], num[h][1] / den[h]);
+      *reinterpret_cast<float2*>(o) = make_float2(num[0] / den, num[1] / den);
     } else {
-      o[0] = num[h][0] / den[h];
+      o[0] = num[0] / den;
     }
   }
 }
@@ -707,7 +682,7 @@ hipError_t launch_s1_b(const DecodeParams& p, int block_size, int group, hipStre
 
 template <int D>
 hipError_t launch_merge_g(const DecodeParams& p, int group, hipStream_t stream) {
-  const dim3 grid((unsigned)(((long long)p.S * p.Hkv + kWavesPerWG - 1) / kWavesPerWG));
+  const dim3 grid((unsigned)(p.head_group == 1 ? p.n_units : p.n_wg));  // one workgroup per worker
   switch (group) {
     case 1: hipLaunchKernelGGL((decode_reduce_shared_kernel<D, 1>), grid, dim3(kThreads), 0, stream, p); break;
     case 2: hipLaunchKernelGGL((decode_reduce_shared_kernel<D, 2>), grid, dim3(kThreads), 0, stream, p); break;
@@ -721,10 +696,9 @@ hipError_t launch_merge_g(const DecodeParams& p, int group, hipStream_t stream) 
 
 }  // namespace
 
-hipError_t launch_shared_prepare(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_shared_prepare(const DecodeParams& p, int head_dim, hipStream_t stream) {
   if (p.S == 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.S + kWavesPerWG - 1) / kWavesPerWG));
-  hipLaunchKernelGGL(shared_prepare_kernel, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(shared_prepare_kernel, dim3((unsigned)p.S), dim3(kThreads), 0, stream, p, head_dim);
   return hipGetLastError();
 }
 

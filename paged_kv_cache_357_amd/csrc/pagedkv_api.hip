@@ -69,8 +69,9 @@ struct Plan {
   size_t pref_bytes = 0; // workspace region of per-sequence chunk and cost prefix sums (balanced)
   size_t share_bytes = 0;  // shared-prefix decode: per-sequence shares with the previous sequence
   size_t grp_bytes = 0;    // shared-prefix decode: group layout for the merge
+  size_t split_bytes = 0;  // shared-prefix decode: per-worker split segments for the merge
   bool shared = false;     // the shared-prefix kernels run this plan
-  size_t total() const { return acc_bytes + ml_bytes + pref_bytes + share_bytes + grp_bytes; }
+  size_t total() const { return acc_bytes + ml_bytes + pref_bytes + share_bytes + grp_bytes + split_bytes; }
 };
 
 // Automatic partition size of the partitioned schedule.  A batch whose
@@ -201,7 +202,8 @@ int plan_shared(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t hea
   sp.acc_bytes = round_up(rows * head_dim * sizeof(float), 256);
   sp.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
   sp.share_bytes = round_up((size_t)num_seqs * sizeof(int32_t), 256);
-  sp.grp_bytes = round_up((4 * (size_t)num_seqs + 4) * sizeof(int32_t), 256);
+  sp.grp_bytes = round_up((3 * (size_t)num_seqs + 4) * sizeof(int32_t), 256);
+  sp.split_bytes = round_up((size_t)waves * sizeof(int32_t), 256);
   *plan = sp;
   return PKV_OK;
 }
@@ -226,6 +228,7 @@ int fill_decode(const Plan& plan, float* out, const void* q, const void* k_cache
   p->ws_pref = ws ? reinterpret_cast<int32_t*>(ws + plan.acc_bytes + plan.ml_bytes) : nullptr;
   p->ws_share = plan.shared ? reinterpret_cast<int32_t*>(ws + plan.acc_bytes + plan.ml_bytes + plan.pref_bytes) : nullptr;
   p->ws_grp = plan.shared ? p->ws_share + plan.share_bytes / sizeof(int32_t) : nullptr;
+  p->ws_split = plan.shared ? p->ws_grp + plan.grp_bytes / sizeof(int32_t) : nullptr;
   p->max_members = plan.shared ? pkv::kSharedCols / (q_heads / kv_heads) : 0;
   p->schedule = plan.schedule;
   p->q = q;
@@ -695,7 +698,7 @@ int paged_attn_decode_shared(float* out, const void* q, void* k_cache, void* v_c
     p.row_b = head_dim * 2 * kv_heads;
   }
   hipError_t e = hipSuccess;
-  if (stages & PKV_STAGE_PREPARE) e = pkv::launch_shared_prepare(p, s);
+  if (stages & PKV_STAGE_PREPARE) e = pkv::launch_shared_prepare(p, head_dim, s);
   if (e == hipSuccess && (stages & PKV_STAGE_ATTEND)) e = pkv::launch_shared_stage1(p, head_dim, block_size, group, s);
   if (e == hipSuccess && (stages & PKV_STAGE_MERGE)) e = pkv::launch_shared_merge(p, head_dim, group, s);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;

@@ -117,7 +117,9 @@ struct DecodeParams {
   float scale_log2;       // scale * log2(e): scores live in the base-2 domain
   // Shared-prefix decode (decode_shared.hip) only:
   int32_t* ws_share;      // [S] tokens sequence s shares with sequence s - 1 (0 for s = 0), prepare stage
-  int32_t* ws_grp;        // group layout for the merge: R, gstart[S+1], gpref[S+1], gcost[S+1], gid[S]
+  int32_t* ws_grp;        // group layout for the merge: R, gstart[S+1], gpref[S+1], gcost[S+1]
+  int32_t* ws_split;      // [workers] the segment (group * head groups + head group) a worker began and
+                          // left to later workers, or -1
   int32_t max_members;    // sequences one group may hold: 16 / G (one matrix-product column per query row)
 };
 
@@ -142,7 +144,7 @@ hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, int group, 
 // Shared-prefix decode launchers (decode_shared.hip): the prepare stage
 // (fused-append rows, prefix shared with the previous sequence), stage 1 and
 // the merge.  bf16 caches only.
-hipError_t launch_shared_prepare(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_shared_prepare(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_shared_stage1(const DecodeParams& p, int head_dim, int block_size, int group, hipStream_t stream);
 hipError_t launch_shared_merge(const DecodeParams& p, int head_dim, int group, hipStream_t stream);
 
