@@ -349,6 +349,33 @@ PKV_API size_t paged_attn_decode_shared_workspace_size(int32_t num_seqs, int32_t
                                                        int32_t max_context_len, int32_t dtype);
 
 /*
+ * paged_attn_decode_noalloc — paged_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results (bitwise: the
+ * same plan and kernels) and errors as paged_attn_decode, without the
+ * workspace: the partial records and prefix sums live in a fixed device array
+ * of PKV_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  The call allocates nothing and calls no allocating routine.
+ *
+ *   - A plan whose workspace (paged_attn_decode_workspace_size with the same
+ *     arguments) exceeds PKV_NOALLOC_SCRATCH_BYTES is rejected with
+ *     PKV_ERR_WORKSPACE before anything is enqueued.
+ *   - The calling thread's current device must be the device of `stream`
+ *     (PKV_ERR_UNSUPPORTED otherwise).  The first call on a device looks up
+ *     the array's device address (hipGetSymbolAddress) and keeps it.
+ *   - Every call on one GPU uses that GPU's one array, and it keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that can
+ *     overlap on one GPU (several streams, several host threads) race on it
+ *     and must be serialised by the caller.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+PKV_API int paged_attn_decode_noalloc(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, int32_t dtype, int32_t partition_size, void* stream);
+
+/*
  * paged_attn_decode_plan — the schedule a call with these arguments uses
  * (partition_size 0 = the automatic choice).  The balanced schedule's worker
  * count follows the compute units of the calling thread's current device (a

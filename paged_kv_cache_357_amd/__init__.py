@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     append_at,
     decode,
     decode_append,
+    decode_noalloc,
     decode_shared,
     DecodeSharedCall,
     shared_workspace_size,
@@ -26,6 +27,7 @@ from ._lib import (  # noqa: F401
     STAGE_ATTEND,
     STAGE_MERGE,
     STAGES_ALL,
+    NOALLOC_SCRATCH_BYTES,
     load_library,
     plan,
     prefill,

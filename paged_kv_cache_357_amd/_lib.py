@@ -37,6 +37,7 @@ SIGNATURES = {
     "paged_attn_decode_append": (_c_int, _DECODE_APPEND_ARGS),
     "paged_attn_decode_append_partitions": (_c_int, _DECODE_APPEND_ARGS),
     "paged_attn_decode_append_reduce": (_c_int, _DECODE_APPEND_ARGS),
+    "paged_attn_decode_noalloc": (_c_int, _DECODE_ARGS[:17] + [_vp]),
     "paged_attn_decode_shared": (_c_int, _DECODE_APPEND_ARGS),
     "paged_attn_decode_shared_workspace_size": (_c_sz, [_c_i32] * 7),
     "paged_attn_decode_plan": (_c_int, [_c_i32] * 8 + [_i32p, _i32p]),
@@ -552,6 +553,25 @@ def decode_shared(q, k_cache, v_cache, block_tables, context_lens, scale, max_co
     once; returns out [S, Hq, D] fp32."""
     return DecodeSharedCall(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, k_new, v_new,
                             out, workspace).run()
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out,
+                   partition_size=0) -> torch.Tensor:
+    """paged_attn_decode_noalloc: the decode with the library's fixed device
+    scratch array instead of a workspace; ``out`` [S, Hq, D] fp32 is given by
+    the caller, and the call allocates nothing."""
+    S, Hq, Hkv, D, B, NB, MB = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    _require(out.shape == (S, Hq, D) and out.dtype == torch.float32, "out must be fp32 [S, Hq, D]")
+    lib = load_library()
+    _check("paged_attn_decode_noalloc",
+           lib.paged_attn_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                         _ptr(context_lens), S, Hq, Hkv, D, B, NB, MB, int(max_context_len),
+                                         float(scale), _DTYPES[q.dtype], int(partition_size), _stream(dev)))
+    return out
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size=0,

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "pagedkv.h"
 #include "pkv_internal.h"
@@ -614,6 +615,76 @@ int paged_attn_decode_append(float* out, const void* q, void* k_cache, void* v_c
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = append_rows_apart(p, s);
   if (e == hipSuccess) e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads, s);
+  if (e == hipSuccess) e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, s);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// ------------------------------------------------------- decode, no allocation
+//
+// paged_attn_decode_noalloc keeps its partial records and prefix sums in this
+// file-scope device array instead of a caller's workspace.  Each GPU holds its
+// own copy for the life of the process.  In host code `scratch` names a host
+// stand-in, not device memory: the kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device and kept here.
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array: the current device, which
+// must be the stream's device.
+static int scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return PKV_ERR_HIP;
+  }
+  if (dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return PKV_ERR_HIP;
+    }
+    if (sdev != dev) return PKV_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return PKV_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+int paged_attn_decode_noalloc(float* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                              int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                              int32_t dtype, int32_t partition_size, void* stream) {
+  // Every host check of paged_attn_decode first, with the whole array as the
+  // workspace (too small a plan fails with PKV_ERR_WORKSPACE before anything
+  // touches the device); then the array's device address.
+  pkv::DecodeParams p;
+  const char* fake = reinterpret_cast<const char*>(256);  // stands in for the address until it is known
+  int st = prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, q_heads, kv_heads,
+                          head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                          partition_size, const_cast<char*>(fake), PKV_NOALLOC_SCRATCH_BYTES, &p);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  st = scratch_for(s, &ws);
+  if (st != PKV_OK) return st;
+  st = prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, q_heads, kv_heads, head_dim,
+                      block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype, partition_size, ws,
+                      PKV_NOALLOC_SCRATCH_BYTES, &p);
+  if (st != PKV_OK) return st;
+  hipError_t e = pkv::launch_decode_partitions(p, dtype, head_dim, block_size, q_heads / kv_heads, s);
   if (e == hipSuccess) e = pkv::launch_decode_reduce(p, head_dim, q_heads / kv_heads, s);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

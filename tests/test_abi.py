@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 33, names
+    assert len(names) == 34, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -129,6 +129,26 @@ def test_decode_append_rejects_before_launch(lib):
         assert f(*args(**ptrs, dtype=5)) == -3
         assert f(*args(**ptrs, maxL=40, P=16)) == -5                      # needs workspace
         assert f(*args(None, None, S=0)) == 0                             # nothing to do
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    """The no-allocation decode runs every host check of paged_attn_decode
+    first, and rejects a plan whose workspace exceeds its fixed scratch array
+    before it looks up the array on the device (so these run on a host with
+    no GPU)."""
+    f = lib.paged_attn_decode_noalloc
+    fake = 0x1000
+    base = _decode_args()
+    del base[17:19]  # no workspace arguments
+    assert f(*base) == -1                                              # null pointers
+    ptrs = [fake] * 6
+    assert f(*(ptrs + base[6:13] + [49] + base[14:])) == -2            # max_context_len > MB * B
+    # partitioned plan of 16-token partitions over 4096 sequences of 32 heads:
+    # 4096 * 32 * 8 partitions * (64 + 2) * 4 bytes > 32 MiB
+    big = ptrs + [4096, 32, 32, 64, 16, 32, 8, 128, 0.125, 0, 16, None]
+    assert pk.workspace_size(4096, 32, 32, 64, 16, 128, 0, 16) > pk.NOALLOC_SCRATCH_BYTES
+    assert f(*big) == -5
+    assert f(*([None] * 6 + [0] + base[7:])) == 0                       # nothing to do
 
 
 def test_append_and_slot_mapping_reject(lib):
