@@ -108,6 +108,11 @@ def parse():
                     help="no GPU run: summarise a rocprofv3 --kernel-trace --stats output folder of this "
                          "workload's run into profiles/ (kernel, calls, mean / min / max duration)")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the copy probe in those runs")
+    ap.add_argument("--flush-sweep", action="store_true",
+                    help="stage 1 of the workload after writing buffers of 0 .. 1024 MiB before each call "
+                         "(median of 10 per size); prints one line and exits")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time the prompt pass alone (--steps flushed repetitions) and print its line")
     return ap.parse_args()
 
 
@@ -503,6 +508,34 @@ def measure_step(pk, torch, w, d, call, reps, warmup, flush, stream_ptr):
             "algorithmic_bytes": "unique" if call == "shared" else "logical"}
 
 
+def measure_prefill(pk, torch, dev, flush, stream_ptr, reps):
+    """The prompt pass at PREFILL_SHAPE: flushed repetitions, median."""
+    from workloads import make_workload, normal_storage
+    ps = PREFILL_SHAPE
+    pw = make_workload("prefill-llama7b", [ps["context"]] * ps["seqs"], ps["q_heads"], ps["kv_heads"],
+                       ps["head_dim"], ps["block_size"], "bf16", 357100)
+    prng = np.random.default_rng(357101)
+    pq = normal_storage(prng, (ps["seqs"] * ps["chunk"], ps["q_heads"], ps["head_dim"]), "bf16").to(dev)
+    pk_, pv_ = pw.k_cache.to(dev), pw.v_cache.to(dev)
+    ptab = torch.from_numpy(pw.block_tables).to(dev)
+    plen = torch.from_numpy(pw.context_lens).to(dev)
+    pstart = torch.arange(0, ps["seqs"] + 1, dtype=torch.int32, device=dev) * ps["chunk"]
+    pout = torch.empty((ps["seqs"] * ps["chunk"], ps["q_heads"], ps["head_dim"]), dtype=torch.float32, device=dev)
+
+    def prefill():
+        pk.prefill(pq, pk_, pv_, ptab, plen, pstart, pw.scale, ps["chunk"], ps["context"], out=pout)
+
+    for _ in range(2):
+        prefill()
+    st = stats(flushed_reps(reps, flush, stream_ptr, lambda: None, prefill, lambda: None))
+    pms = st["median_ms"]
+    flops = prefill_flops(ps["seqs"], ps["chunk"], ps["context"], ps["q_heads"], ps["head_dim"])
+    tf = flops / (pms / 1e3) / 1e12
+    return {"kernel": "prefill_kernel", "shape": ps, "flops": flops, "ms": pms, "times": st, "TFLOPs": tf,
+            "bound": "mfma", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+            "tokens_per_s": ps["seqs"] * ps["chunk"] / (pms / 1e3)}
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -515,6 +548,17 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path (the decode shards over "
               "sequences or kv heads with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.prefill_only:
+        import torch
+        import paged_kv_cache_357_amd as pk
+        pk.load_library()
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        res = measure_prefill(pk, torch, dev, flush, torch.cuda.current_stream(dev).cuda_stream, args.steps)
+        print(json.dumps({"prefill": res}), flush=True)
+        return
 
     from workloads import make_config
     k = WORKLOADS[args.workload]
@@ -540,6 +584,26 @@ def main():
     stream_ptr = torch.cuda.current_stream(dev).cuda_stream  # the stream every entry point launches on
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     print(f"[bench] {args.workload} call {args.call}: warm-up", file=sys.stderr, flush=True)
+    if args.flush_sweep:
+        for _ in range(5):
+            st.run()
+        torch.cuda.synchronize()
+        res = {}
+        for mib in (0, 8, 24, 48, 96, 192, 320, 512, 1024):
+            buf = flush[: mib << 20]
+            ms = flushed_reps(12, buf, stream_ptr, lambda: None, st.stage1, lambda: None) if mib else None
+            if ms is None:  # warm: back to back, no write in between
+                ev = HipEvents(24, stream_ptr)
+                for i in range(12):
+                    ev.record(2 * i)
+                    st.stage1()
+                    ev.record(2 * i + 1)
+                torch.cuda.synchronize()
+                ms = [ev.ms(2 * i, 2 * i + 1) for i in range(12)]
+                ev.close()
+            res[mib] = float(np.median(ms[2:])) * 1e3
+        print(json.dumps({"workload": args.workload, "call": args.call, "stage1_us_by_flush_mib": res}), flush=True)
+        return
 
     for _ in range(args.warmup):
         st.run()
@@ -587,8 +651,7 @@ def main():
         "timing": "median of K steps, each after writing a 1 GiB buffer, HIP events on the launch stream",
         "step": step,
         "stage1": {**s1, "bracket": {"shared": "stage 1 kernel alone (prepare and merge outside the events)",
-                                     "fused": "stage-1 call (with the matrix-core kernels it also writes the "
-                                              "new rows in a launch of its own)",
+                                     "fused": "stage 1 kernel alone (it writes the new rows itself)",
                                      "two-launch": "stage 1 kernel alone"}[args.call]},
         "timed_region_s": region_s,
         "warm_back_to_back_ms_per_step": warm_ms,
@@ -722,32 +785,7 @@ def main():
                                         "in_GBps": moved / (in_ms / 1e3) / 1e9}
             del hk, hv, staging
 
-        from workloads import make_workload, normal_storage
-        ps = PREFILL_SHAPE
-        pw = make_workload("prefill-llama7b", [ps["context"]] * ps["seqs"], ps["q_heads"], ps["kv_heads"],
-                           ps["head_dim"], ps["block_size"], "bf16", 357100)
-        prng = np.random.default_rng(357101)
-        pq = normal_storage(prng, (ps["seqs"] * ps["chunk"], ps["q_heads"], ps["head_dim"]), "bf16").to(dev)
-        pk_, pv_ = pw.k_cache.to(dev), pw.v_cache.to(dev)
-        ptab = torch.from_numpy(pw.block_tables).to(dev)
-        plen = torch.from_numpy(pw.context_lens).to(dev)
-        pstart = torch.arange(0, ps["seqs"] + 1, dtype=torch.int32, device=dev) * ps["chunk"]
-        pout = torch.empty((ps["seqs"] * ps["chunk"], ps["q_heads"], ps["head_dim"]), dtype=torch.float32,
-                           device=dev)
-
-        def prefill():
-            pk.prefill(pq, pk_, pv_, ptab, plen, pstart, pw.scale, ps["chunk"], ps["context"], out=pout)
-
-        for _ in range(2):
-            prefill()
-        pms = stats(flushed_reps(reps, flush, stream_ptr, lambda: None, prefill, lambda: None))["median_ms"]
-        flops = prefill_flops(ps["seqs"], ps["chunk"], ps["context"], ps["q_heads"], ps["head_dim"])
-        tf = flops / (pms / 1e3) / 1e12
-        extra["prefill"] = {"kernel": "prefill_kernel", "shape": ps, "flops": flops, "ms": pms, "TFLOPs": tf,
-                            "bound": "mfma", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
-                            "frac": tf / MFMA_BF16_PEAK_TFLOPS,
-                            "tokens_per_s": ps["seqs"] * ps["chunk"] / (pms / 1e3)}
-        del pq, pk_, pv_, pout, pw
+        extra["prefill"] = measure_prefill(pk, torch, dev, flush, stream_ptr, reps)
 
     if args.copy_probe_mib:
         import ctypes

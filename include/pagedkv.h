@@ -226,12 +226,8 @@ PKV_API int paged_attn_decode_reduce(float* out, const void* q, const void* k_ca
  *   out[s,h,:] = paged_attn_decode over positions 0 .. L
  *
  * The result equals paged_kv_append_at(positions = context_lens) followed by
- * paged_attn_decode with context_lens + 1, bitwise.  With the vector-ALU
- * kernels (fp32, or bf16 with fewer than 4 query heads per kv head) under
- * the balanced schedule, and with the partitioned schedule, stage 1 writes
- * the new rows itself, one launch fewer; with the matrix-core kernels the
- * call writes them with a launch of its own before stage 1 (measured
- * faster for those kernels).
+ * paged_attn_decode with context_lens + 1, bitwise.  Stage 1 writes the new
+ * rows itself (no launch of their own).
  *
  *   k_cache, v_cache [num_blocks, block_size, kv_heads, head_dim] dtype, in/out:
  *                the new rows are written, nothing else.
@@ -338,9 +334,8 @@ PKV_API int paged_attn_decode_shared(float* out, const void* q, void* k_cache, v
  * paged_attn_decode_shared_workspace_size — bytes of workspace
  * paged_attn_decode_shared needs for these arguments (same current device as
  * the call).  Shared-prefix kernels: partial records for W worker waves (two
- * records of 16 rows of head_dim + 2 floats each), num_seqs ints of shares,
- * 3 * num_seqs + 4 ints of group layout and W ints of split segments, each
- * rounded up to 256 bytes;
+ * records of 16 rows of head_dim + 2 floats each), num_seqs ints of shares
+ * and 4 W ints of split segments, each rounded up to 256 bytes;
  * otherwise paged_attn_decode_workspace_size with partition_size 0.  Host
  * only; 0 for arguments the call would reject.
  */

@@ -56,9 +56,9 @@
 //
 // Fused append (paged_attn_decode_append): the lengths are those before the
 // append, L + 1 tokens are attended, and each sequence's new K/V row goes to
-// position L.  The balanced vector-ALU kernel loads the row ahead through its
-// pipeline, keeps it in LDS, substitutes it for the slot's old contents in the
-// segment's last chunk and writes it to the pool after its last chunk; the
+// position L.  The balanced kernel (either core) loads the row ahead through
+// its pipeline, keeps it in LDS, substitutes it for the slot's old contents in
+// the segment's last chunk and writes it to the pool after its last chunk; the
 // partitioned kernel writes it before its first load.
 //
 // Masking: rows at or beyond a piece's end inside its last chunk read as zero

@@ -76,15 +76,29 @@ __global__ __launch_bounds__(kThreads) void shared_prepare_kernel(DecodeParams a
     const int blk = a.tables[(size_t)s * a.MB + L / B];
     if (blk >= 0 && blk < a.NB) {
       const size_t dst = ((size_t)blk * B + (size_t)(L % B)) * (size_t)a.row_b;
-      const uint4* kn = reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + (size_t)s * a.row_b);
-      const uint4* vn = reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + (size_t)s * a.row_b);
-      uint4* kd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst);
-      uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst);
-      for (int i = tid; i < a.row_b / 16; i += kThreads) {
-        const uint4 kv = kn[i];
-        const uint4 vv = vn[i];
-        kd[i] = kv;
-        vd[i] = vv;
+      const uint4* __restrict__ kn =
+          reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + (size_t)s * a.row_b);
+      const uint4* __restrict__ vn =
+          reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + (size_t)s * a.row_b);
+      uint4* __restrict__ kd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst);
+      uint4* __restrict__ vd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst);
+      const int n16 = a.row_b / 16;
+      for (int i = tid; i < n16; i += 2 * kThreads) {  // both halves' loads in flight before any store
+        const int i2 = i + kThreads;
+        const bool two = i2 < n16;
+        const uint4 k0 = kn[i];
+        const uint4 v0 = vn[i];
+        uint4 k1 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+        if (two) {
+          k1 = kn[i2];
+          v1 = vn[i2];
+        }
+        kd[i] = k0;
+        vd[i] = v0;
+        if (two) {
+          kd[i2] = k1;
+          vd[i2] = v1;
+        }
       }
     }
   }
@@ -268,18 +282,6 @@ void decode_shared_kernel(DecodeParams a) {
     gcost[R] = T_cost;
   }
   __syncthreads();
-  if (blockIdx.x == 0) {  // the group layout, for the merge
-    int* gs = a.ws_grp + 1;
-    int* gp = gs + S + 1;
-    int* gc = gp + S + 1;
-    if (tid == 0) a.ws_grp[0] = R;
-    for (int i = tid; i <= R; i += kThreads) {
-      gs[i] = gstart[i];
-      gp[i] = gpref[i];
-      gc[i] = gcost[i];
-    }
-  }
-
   // ---- this worker's share (see the balanced schedule of decode.hip)
   const int Hkv = a.Hkv;
   const int HG = a.head_group;
@@ -287,12 +289,24 @@ void decode_shared_kernel(DecodeParams a) {
   const int Ru = uniform(R);
   const long long T = (long long)NGR * uniform(T_chunks);
   const int ell = logical_workgroup(blockIdx.x, a.xcd_group, a.n_wg, a.xcds);
-  if (ell < 0 || T == 0) return;
+  if (ell < 0) return;
   const int w = ell * kWavesPerWG + wave;  // this wave's partial-record slots
   const int worker = HG == 1 ? w : ell;
-  const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
-  if (worker >= W_eff) return;
   const int hsub = HG == 1 ? 0 : wave;
+  // What the merge reads of this worker: the segment it began and left to
+  // later workers (or -1), that segment's first member, columns and last worker.
+  auto put_split = [&](int4 v) {
+    if (hsub == 0 && lane == 0) reinterpret_cast<int4*>(a.ws_split)[worker] = v;
+  };
+  if (T == 0) {
+    put_split(make_int4(-1, 0, 0, 0));
+    return;
+  }
+  const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
+  if (worker >= W_eff) {
+    put_split(make_int4(-1, 0, 0, 0));
+    return;
+  }
   const long long TC = (long long)NGR * uniform(T_cost);
   auto last_group_at = [&](const int* pre, long long x) {  // last r with NGR * pre[r] <= x
     int ra = 0, rb = Ru;
@@ -321,11 +335,10 @@ void decode_shared_kernel(DecodeParams a) {
   // segment is the prefix's chunk j for j < P / 16, then the tails of the
   // members in order.  part = -1 in the prefix, else the member index.
   struct Cursor {
-    int r, g, j, n, a0, nm, P, part, pos;
+    int r, g, j, n, a0, nm, P, part, pos, end;  // end: of the current run (P, or the member's length)
   };
-  // member whose table the chunk is read through, and the end of its run
+  // member whose table the chunk is read through
   auto row_of = [&](const Cursor& c) { return c.a0 + (c.part < 0 ? 0 : c.part); };
-  auto end_of = [&](const Cursor& c) { return c.part < 0 ? c.P : uniform(slen[c.a0 + c.part]); };
   auto tail_chunks = [&](int m, int P) { return (max(uniform(slen[m]) - P, 0) + kChunk - 1) / kChunk; };
   auto enter = [&](Cursor& c, int r) {
     c.r = r;
@@ -340,6 +353,7 @@ void decode_shared_kernel(DecodeParams a) {
     if (j < np) {
       c.part = -1;
       c.pos = j * kChunk;
+      c.end = c.P;
       return;
     }
     j -= np;
@@ -351,15 +365,18 @@ void decode_shared_kernel(DecodeParams a) {
     }
     c.part = k;
     c.pos = c.P + j * kChunk;
+    c.end = uniform(slen[c.a0 + k]);
   };
   auto advance = [&](Cursor& c) {
     if (++c.j < c.n) {
       c.pos += kChunk;
-      if (c.pos >= end_of(c)) {  // the next member whose tail holds tokens
+      if (c.pos >= c.end) {  // the next member whose tail holds tokens
         int k = c.part + 1;
-        while (k < c.nm - 1 && uniform(slen[c.a0 + k]) <= c.P) ++k;
+        int e = uniform(slen[c.a0 + k]);
+        while (k < c.nm - 1 && e <= c.P) e = uniform(slen[c.a0 + ++k]);
         c.part = k;
         c.pos = c.P;
+        c.end = e;
       }
       return;
     }
@@ -444,7 +461,7 @@ void decode_shared_kernel(DecodeParams a) {
           ((size_t)(ok ? id : 0) * B + (size_t)(ic.pos % B)) * rs + (size_t)(ic.g * HG + hsub) * ROW;
       kc = kpool + cbase;
       vc = vpool + cbase;
-      nbytes = ok ? (uint32_t)min(kChunk - 1, end_of(ic) - 1 - ic.pos) * rs + ROW : 0u;
+      nbytes = ok ? (uint32_t)min(kChunk - 1, ic.end - 1 - ic.pos) * rs + ROW : 0u;
       next_entry(b.app);
       --to_issue;
       if (to_issue > 0) advance(ic);
@@ -502,7 +519,7 @@ void decode_shared_kernel(DecodeParams a) {
       col_bad = false;
       first_consume = false;
     }
-    const int lim = min(kChunk - 1, end_of(cc) - 1 - cc.pos);
+    const int lim = min(kChunk - 1, cc.end - 1 - cc.pos);
     const bool seg_end = (cc.j == cc.n - 1);
     const bool col_on = cc.part < 0 ? (cl < cc.nm * G) : (cl / G == cc.part);
     core.consume(lim, a.scale_log2, cur, col_on);
@@ -559,91 +576,102 @@ void decode_shared_kernel(DecodeParams a) {
     for (int k = 0; k < NB; ++k) step(buf[k], bad[k], buf[(k + NB - 1) % NB], bad[(k + NB - 1) % NB]);
   }
   flush();
-  if (hsub == 0 && lane == 0) a.ws_split[worker] = split;
+  int4 rec = make_int4(-1, 0, 0, 0);
+  if (split >= 0) {  // the last piece began cc's segment, which later workers continue
+    const long long cbase =
+        (long long)NGR * uniform(gcost[cc.r]) + (long long)cc.g * (cc.n + kSegCost) + kSegCost;
+    rec = make_int4(split, cc.a0, cc.nm * G, (int)balanced_wave_of(cbase + cc.n - 1, TC, W_eff));
+  }
+  put_split(rec);
 }
 
 // ------------------------------------------------------------------ merge
 
-// One workgroup per worker w: if w began a segment (group r, head group gg)
-// that later workers continued, the pieces of workers w .. w1 are merged into
-// the segment's rows (every column of its HG kv heads), in worker order:
-// M the largest piece max, rows sum(exp2(m_p - M) acc_p) / sum(exp2(m_p - M)
-// l_p).  A segment one worker finished was written by stage 1; the rows of
-// empty and invalid sequences by the prepare stage.  A workspace that does
-// not hold this call's stage-1 layout (no stage 1 before the merge) makes
-// the kernel write nothing rather than read out of place.
+// Workgroup (w0, y), one wave per row: if worker w0 began a segment (group,
+// head group gg) that later workers continued, wave i merges row y * 4 + i of
+// the segment's HG * columns rows (kv head gg * HG + row / columns, column
+// row % columns) from the pieces of workers w0 .. w1, in worker order, eight
+// pieces' loads in flight at a time: with M the largest piece max so far,
+// sum(exp2(m_p - M) acc_p) / sum(exp2(m_p - M) l_p).  Stage 1 leaves, per
+// worker, the segment id, its first member, its columns and its last worker.
+// A segment one worker finished was written by stage 1; the rows of empty
+// and invalid sequences by the prepare stage.  A record that does not fit
+// the call (no stage 1 before the merge) makes the kernel write nothing
+// rather than read out of place.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_reduce_shared_kernel(DecodeParams a) {
   constexpr int CPL = D / 64;  // columns per lane (1 or 2)
+  constexpr int KB = 8;        // pieces loaded together
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int w0 = (int)blockIdx.x;
-  const int S = a.S;
   const int HG = a.head_group;
   const int NGR = a.Hkv / HG;
-  const int* gs = a.ws_grp + 1;
-  const int* gp = gs + S + 1;
-  const int* gc = gp + S + 1;
-  const int R = a.ws_grp[0];
-  if (R < 1 || R > S) return;
-  const long long T = (long long)NGR * gp[R];
-  const long long TC = (long long)NGR * gc[R];
-  if (T <= 0 || TC <= 0) return;
-  const long long W_eff = balanced_workers(T, HG == 1 ? a.n_units : a.n_wg);
-  if (w0 >= W_eff) return;
-  const int split = a.ws_split[w0];
+  const int workers = HG == 1 ? a.n_units : a.n_wg;
+  const int4 rec = reinterpret_cast<const int4*>(a.ws_split)[w0];
+  const int split = uniform(rec.x);
   if (split < 0) return;
-  const int r = split / NGR;
-  const int gg = split - r * NGR;
-  const int a0 = r < R ? gs[r] : 0;
-  const int nm = r < R ? gs[r + 1] - a0 : 0;
-  const int n = r < R ? gp[r + 1] - gp[r] : 0;
-  const long long cbase = (long long)NGR * (r < R ? gc[r] : 0) + (long long)gg * (n + kSegCost) + kSegCost;
-  const long long w1 = balanced_wave_of(cbase + n - 1, TC, W_eff);
-  const bool ok = r < R && nm >= 1 && nm * G <= kSharedCols && n > 0 && balanced_wave_of(cbase, TC, W_eff) == w0 &&
-                  w1 > w0 && w1 < W_eff;
-  if (!ok) return;
-  const int pieces = (int)(w1 - w0 + 1);
-  const int ncols = nm * G;
-  // rows: (head of the group hsub, column c), taken by the waves in turn
-  for (int row = wave; row < HG * ncols; row += kWavesPerWG) {
-    const int hsub = row / ncols;
-    const int c = row - hsub * ncols;
-    const int s = a0 + c / G;
-    const int kvh = gg * HG + hsub;
-    auto piece_row = [&](int p) -> size_t {
-      const size_t wave_id = HG == 1 ? (size_t)(w0 + p) : (size_t)(w0 + p) * kWavesPerWG + hsub;
-      return (wave_id * 2 + (p == 0 ? 1 : 0)) * kSharedCols + (size_t)c;
-    };
-    float M = kNegBig;
-    for (int p0 = 0; p0 < pieces; p0 += 64) {
-      const int p = p0 + lane;
-      if (p < pieces) M = fmaxf(M, a.ws_ml[piece_row(p)].x);
-    }
+  const int a0 = uniform(rec.y);
+  const int ncols = uniform(rec.z);
+  const int w1 = uniform(rec.w);
+  const int gg = split % NGR;
+  if (ncols < 1 || ncols > kSharedCols || a0 < 0 || a0 + (ncols - 1) / G >= a.S || w1 <= w0 || w1 >= workers)
+    return;
+  const int row = (int)blockIdx.y * kWavesPerWG + wave;
+  if (row >= HG * ncols) return;
+  const int hsub = row / ncols;
+  const int c = row - hsub * ncols;
+  const int s = a0 + c / G;
+  const int kvh = gg * HG + hsub;
+  const int pieces = w1 - w0 + 1;
+  auto piece_row = [&](int p) -> size_t {
+    const size_t wave_id = HG == 1 ? (size_t)(w0 + p) : (size_t)(w0 + p) * kWavesPerWG + hsub;
+    return (wave_id * 2 + (p == 0 ? 1 : 0)) * kSharedCols + (size_t)c;
+  };
+  float M = kNegBig, den = 0.0f, num[CPL];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float num[CPL], den = 0.0f;
+  for (int j = 0; j < CPL; ++j) num[j] = 0.0f;
+  for (int p0 = 0; p0 < pieces; p0 += KB) {
+    float2 t[KB];
+    float x[KB][CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) num[j] = 0.0f;
-    for (int p = 0; p < pieces; ++p) {
-      const size_t rr = piece_row(p);
-      const float2 t = a.ws_ml[rr];
-      const float f = fast_exp2(t.x - M);
-      den = fmaf(t.y, f, den);
+    for (int i = 0; i < KB; ++i) {
+      const bool in = p0 + i < pieces;
+      const size_t rr = piece_row(in ? p0 + i : p0);
+      t[i] = in ? a.ws_ml[rr] : make_float2(kNegBig, 0.0f);
       if constexpr (CPL == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(a.ws_acc + rr * D + lane * CPL);
-        num[0] = fmaf(v.x, f, num[0]);
-        num[1] = fmaf(v.y, f, num[1]);
+        const float2 v = in ? *reinterpret_cast<const float2*>(a.ws_acc + rr * D + lane * CPL) : make_float2(0.0f, 0.0f);
+        x[i][0] = v.x;
+        x[i][1] = v.y;
       } else {
-        num[0] = fmaf(a.ws_acc[rr * D + lane], f, num[0]);
+        x[i][0] = in ? a.ws_acc[rr * D + lane] : 0.0f;
       }
     }
-    float* o = a.out + ((size_t)s * a.Hq + (size_t)kvh * G + (size_t)(c % G)) * D + lane * CPL;
-    if constexpr (CPL == 2) {
-      *reinterpret_cast<float2*>(o) = make_float2(num[0] / den, num[1] / den);
-    } else {
-      o[0] = num[0] / den;
+    float Mn = M;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) Mn = fmaxf(Mn, t[i].x);
+    if (p0 > 0) {  // a later batch with a larger max rescales the sums so far
+      const float sc = fast_exp2(M - Mn);
+      den *= sc;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) num[j] *= sc;
     }
+    M = Mn;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if (p0 + i < pieces) {
+        const float f = fast_exp2(t[i].x - M);
+        den = fmaf(t[i].y, f, den);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) num[j] = fmaf(x[i][j], f, num[j]);
+      }
+    }
+  }
+  float* o = a.out + ((size_t)s * a.Hq + (size_t)kvh * G + (size_t)(c % G)) * D + lane * CPL;
+  if constexpr (CPL == 2) {
+    *reinterpret_cast<float2*>(o) = make_float2(num[0] / den, num[1] / den);
+  } else {
+    o[0] = num[0] / den;
   }
 }
 
@@ -682,7 +710,8 @@ hipError_t launch_s1_b(const DecodeParams& p, int block_size, int group, hipStre
 
 template <int D>
 hipError_t launch_merge_g(const DecodeParams& p, int group, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.head_group == 1 ? p.n_units : p.n_wg));  // one workgroup per worker
+  // (worker, slice of four rows of the worker's split segment: HG * 16 rows at most)
+  const dim3 grid((unsigned)(p.head_group == 1 ? p.n_units : p.n_wg), (unsigned)(p.head_group * kSharedCols / kWavesPerWG));
   switch (group) {
     case 1: hipLaunchKernelGGL((decode_reduce_shared_kernel<D, 1>), grid, dim3(kThreads), 0, stream, p); break;
     case 2: hipLaunchKernelGGL((decode_reduce_shared_kernel<D, 2>), grid, dim3(kThreads), 0, stream, p); break;

