@@ -157,6 +157,42 @@ __device__ int block_excl_sum(int v, int* tmp, int* total) {
   return run;
 }
 
+// Two exclusive prefix sums at once (one pair of barriers); tmp holds
+// 2 * kWavesPerWG ints.
+__device__ int2 block_excl_sum2(int v, int u, int* tmp, int* total_v, int* total_u) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int iv = v, iu = u;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int tv = __shfl_up(iv, off);
+    const int tu = __shfl_up(iu, off);
+    if (lane >= off) {
+      iv += tv;
+      iu += tu;
+    }
+  }
+  if (lane == 63) {
+    tmp[wave] = iv;
+    tmp[kWavesPerWG + wave] = iu;
+  }
+  __syncthreads();
+  int rv = iv - v, ru = iu - u, sv = 0, su = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerWG; ++w) {
+    if (w < wave) {
+      rv += tmp[w];
+      ru += tmp[kWavesPerWG + w];
+    }
+    sv += tmp[w];
+    su += tmp[kWavesPerWG + w];
+  }
+  __syncthreads();
+  *total_v = sv;
+  *total_u = su;
+  return make_int2(rv, ru);
+}
+
 // Largest v among the threads before this one (-1 if none).
 __device__ int block_excl_max(int v, int* tmp) {
   const int lane = threadIdx.x & 63;
@@ -189,7 +225,7 @@ void decode_shared_kernel(DecodeParams a) {
   constexpr int NM = kSharedCols / G;  // members a group may hold
   extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ __attribute__((aligned(16))) char s_stage[kWavesPerWG][Core::kStageBytes];
-  __shared__ int s_tmp[kWavesPerWG];
+  __shared__ int s_tmp[2 * kWavesPerWG];
 
   const int S = a.S;
   const int tid = threadIdx.x;
@@ -211,15 +247,31 @@ void decode_shared_kernel(DecodeParams a) {
   const int per = (S + kThreads - 1) / kThreads;
   const int s_lo = min(S, tid * per);
   const int s_hi = min(S, s_lo + per);
-  int last_break = -1;
-  for (int s = s_lo; s < s_hi; ++s) slen[s] = max(shared_attended_len(a, s), 0);
+  // Lengths and shares in one round of loads (global address space: the
+  // loads need not wait for the LDS stores in between).
+  {
+    typedef __attribute__((address_space(1))) const int32_t g_i32;
+    g_i32* glens = (g_i32*)a.lens;
+    g_i32* gshare = (g_i32*)a.ws_share;
+    static_assert(kBalancedMaxSeqs % kThreads == 0, "a thread's range of sequences is at most this long");
+#pragma unroll
+    for (int i = 0; i < kBalancedMaxSeqs / kThreads; ++i) {
+      const int s = s_lo + i;
+      if (s < s_hi) {
+        const int L = glens[s];
+        const int La = a.append ? ((L >= 0 && L < a.max_len) ? L + 1 : -1) : ((L >= 0 && L <= a.max_len) ? L : -1);
+        slen[s] = max(La, 0);
+        shv[s] = s > 0 ? gshare[s] : 0;
+      }
+    }
+  }
   __syncthreads();
+  int last_break = -1;
   for (int s = s_lo; s < s_hi; ++s) {
     // A share never exceeds what both sequences held before the append, so
     // a prefix is only ever read within each member's own tokens.
-    int sh = s > 0 ? a.ws_share[s] : 0;
     const int held = s > 0 ? min(slen[s], slen[s - 1]) - a.append : 0;
-    sh = max(0, min(sh, held)) & ~(kChunk - 1);
+    const int sh = max(0, min(shv[s], held)) & ~(kChunk - 1);
     shv[s] = sh;
     if (sh <= 0) last_break = s;
   }
@@ -268,8 +320,8 @@ void decode_shared_kernel(DecodeParams a) {
     c_loc += n > 0 ? n + kSegCost : 0;
   }
   int T_chunks = 0, T_cost = 0;
-  int nb = block_excl_sum(n_loc, s_tmp, &T_chunks);
-  int cb = block_excl_sum(c_loc, s_tmp, &T_cost);
+  const int2 ncb = block_excl_sum2(n_loc, c_loc, s_tmp, &T_chunks, &T_cost);
+  int nb = ncb.x, cb = ncb.y;
   for (int r = r_lo; r < r_hi; ++r) {
     const int n = gpref[r];
     gpref[r] = nb;
