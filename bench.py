@@ -108,6 +108,12 @@ def parse():
                     help="no GPU run: summarise a rocprofv3 --kernel-trace --stats output folder of this "
                          "workload's run into profiles/ (kernel, calls, mean / min / max duration)")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the copy probe in those runs")
+    ap.add_argument("--write-pmc", nargs="+", metavar="DIR_OR_NAME",
+                    help="no GPU run: rocprofv3 --pmc output folders, then a summary name; writes the mean per "
+                         "dispatch of every counter of --pmc-kernel to profiles/NAME.txt")
+    ap.add_argument("--pmc-kernel", default="prefill_kernel", help="kernel name pattern for --write-pmc")
+    ap.add_argument("--pmc-command", default="python bench.py --prefill-only --steps 5",
+                    help="the profiled command, recorded in the --write-pmc summary")
     ap.add_argument("--flush-sweep", action="store_true",
                     help="stage 1 of the workload after writing buffers of 0 .. 1024 MiB before each call "
                          "(median of 10 per size); prints one line and exits")
@@ -308,6 +314,45 @@ fetch_over_logical: {fetch_b / logical:.4f}
 fetch_over_unique: {fetch_b / unique:.4f}
 """
     with open(traffic_file(args.workload, args.call), "w") as f:
+        f.write(text)
+    print(text)
+
+
+def write_pmc(args):
+    """Mean per dispatch of every counter in rocprofv3 --pmc output folders,
+    for the kernels whose name contains --pmc-kernel, into profiles/."""
+    import csv
+    import glob
+    folders, name = args.write_pmc[:-1], args.write_pmc[-1]
+    acc = {}
+    per_folder = {}
+    for folder in folders:
+        for path in glob.glob(os.path.join(folder, "**", "*counter_collection*.csv"), recursive=True):
+            with open(path, newline="") as f:
+                for r in csv.DictReader(f):
+                    per_folder.setdefault(folder, set()).add(r["Counter_Name"])
+                    if args.pmc_kernel in r["Kernel_Name"]:
+                        key = (folder, r.get("Dispatch_Id", ""))
+                        acc.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+                        acc[key][r["Counter_Name"]] += float(r["Counter_Value"])
+    if not acc:
+        raise SystemExit(f"no dispatch of {args.pmc_kernel} under {folders}")
+    names = sorted({c for v in acc.values() for c in v})
+    mean = {c: float(np.mean([v[c] for v in acc.values() if c in v])) for c in names}
+    lines = [f"# rocprofv3 counters of {args.pmc_kernel}, mean per dispatch over the listed runs, MI355X",
+             "# (counters summed over the rows of a dispatch: XCDs / shader engines / SIMDs as the tool reports)",
+             "#", "#   cd /tmp && export TMPDIR=/tmp && cd <repository root> &&"]
+    for folder in folders:
+        counters = " ".join(sorted(per_folder.get(folder, ())))
+        lines.append(f"#   timeout -s KILL 90 rocprofv3 --pmc {counters} "
+                     f"-d {folder} -o run --output-format csv -- {args.pmc_command}")
+    lines.append(f"#   python bench.py --pmc-kernel {args.pmc_kernel} --pmc-command '{args.pmc_command}' "
+                 f"--write-pmc {' '.join(folders)} {name}")
+    lines.append("")
+    for c in names:
+        lines.append(f"{c}: {mean[c]:.6g}")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(PROFILES, f"{name}.txt"), "w") as f:
         f.write(text)
     print(text)
 
@@ -543,6 +588,9 @@ def main():
         return
     if args.write_traces:
         write_traces(args)
+        return
+    if args.write_pmc:
+        write_pmc(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (the decode shards over "

@@ -32,12 +32,12 @@ def _inputs(lens, n_new, hq, hkv, D, B, seed):
     return w, q_start, q
 
 
-def _gpu(pk, w, q_start, q, lens=None, max_q=None, max_len=None):
+def _gpu(pk, w, q_start, q, lens=None, max_q=None, max_len=None, scale=None):
     lens = w.context_lens if lens is None else lens
     n = np.diff(q_start)
     out = pk.prefill(q.cuda(), w.k_cache.cuda(), w.v_cache.cuda(), torch.from_numpy(w.block_tables).cuda(),
                      torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda(),
-                     torch.from_numpy(q_start).cuda(), w.scale,
+                     torch.from_numpy(q_start).cuda(), w.scale if scale is None else scale,
                      int(n.max()) if max_q is None else max_q,
                      int(np.max(lens)) if max_len is None else max_len)
     torch.cuda.synchronize()
@@ -72,6 +72,19 @@ def test_prefill_matches_oracle(pk, case):
     want = oracle_prefill(raw_numpy(q), raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables,
                           w.context_lens, q_start, w.scale, "bf16", B)
     _check(got, want, what=f"case {case}")
+
+
+@pytest.mark.parametrize("case", [0, 1, 3])
+def test_prefill_negative_scale(pk, case):
+    """A negative scale (the kernel carries its sign on q) and a scale of
+    several units, against the oracle with the same scale."""
+    lens, n_new, hq, hkv, D, B = CASES[case]
+    w, q_start, q = _inputs(lens, n_new, hq, hkv, D, B, 40 + case)
+    for scale in (-w.scale, float(np.float32(-0.75)), float(np.float32(2.5 * w.scale))):
+        got = _gpu(pk, w, q_start, q, scale=scale)
+        want = oracle_prefill(raw_numpy(q), raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables,
+                              w.context_lens, q_start, scale, "bf16", B)
+        _check(got, want, what=f"case {case} scale {scale}")
 
 
 def test_prefill_last_rows_equal_decode(pk):
