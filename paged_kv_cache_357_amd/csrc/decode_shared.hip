@@ -63,42 +63,60 @@ __device__ __forceinline__ int shared_attended_len(const DecodeParams& a, int s)
 
 // One workgroup per sequence s: the fused-append row, the rows of a sequence
 // with nothing to attend to (zeros for L = 0, NaN for a length the launch
-// cannot cover; no later stage writes them), and the share with s - 1.
+// cannot cover; no later stage writes them), and the share with s - 1.  The
+// loads come in two dependent rounds: the new rows and both lengths, then
+// the slot's table entry and the first 64 entries of both tables.
 __global__ __launch_bounds__(kThreads) void shared_prepare_kernel(DecodeParams a, int head_dim) {
   const int s = (int)blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int B = a.block_size;
+  constexpr int kRowRegs = 4;  // 16-byte pieces a thread holds: rows up to 16 KiB
+  const int n16 = a.row_b / 16;
+  const bool held = a.append && n16 <= kRowRegs * kThreads;
+  const uint4* __restrict__ kn =
+      reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + (size_t)s * a.row_b);
+  const uint4* __restrict__ vn =
+      reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + (size_t)s * a.row_b);
+  // round 1
+  uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0, k2 = k0, k3 = k0, v0 = k0, v1 = k0, v2 = k0, v3 = k0;
+  if (held) {
+    if (tid < n16) { k0 = kn[tid]; v0 = vn[tid]; }
+    if (tid + kThreads < n16) { k1 = kn[tid + kThreads]; v1 = vn[tid + kThreads]; }
+    if (tid + 2 * kThreads < n16) { k2 = kn[tid + 2 * kThreads]; v2 = vn[tid + 2 * kThreads]; }
+    if (tid + 3 * kThreads < n16) { k3 = kn[tid + 3 * kThreads]; v3 = vn[tid + 3 * kThreads]; }
+  }
   const int L = a.lens[s];
   const int La = shared_attended_len(a, s);
-  if (a.append && La > 0) {
+  const bool pair = s > 0 && La >= 0 && shared_attended_len(a, s - 1) >= 0;
+  // round 2: the slot's block; the tables of s - 1 and s (shared tokens are
+  // counted within the tokens both held before this step's append)
+  const int m = pair ? min(L, a.lens[s - 1]) : 0;
+  const int nb = (m + B - 1) / B;
+  const int32_t* t0 = a.tables + (size_t)(s > 0 ? s - 1 : 0) * a.MB;
+  const int32_t* t1 = a.tables + (size_t)s * a.MB;
+  int e0 = 0, e1 = 0;
+  if (tid < 64 && lane < nb) {
+    e0 = t0[lane];
+    e1 = t1[lane];
+  }
+  const int blk = (a.append && La > 0) ? a.tables[(size_t)s * a.MB + L / B] : -1;
+  if (blk >= 0 && blk < a.NB) {
     // the new token's K and V rows (all kv heads) into slot T[L / B] * B + L % B
-    const int blk = a.tables[(size_t)s * a.MB + L / B];
-    if (blk >= 0 && blk < a.NB) {
-      const size_t dst = ((size_t)blk * B + (size_t)(L % B)) * (size_t)a.row_b;
-      const uint4* __restrict__ kn =
-          reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + (size_t)s * a.row_b);
-      const uint4* __restrict__ vn =
-          reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + (size_t)s * a.row_b);
-      uint4* __restrict__ kd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst);
-      uint4* __restrict__ vd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst);
-      const int n16 = a.row_b / 16;
-      for (int i = tid; i < n16; i += 2 * kThreads) {  // both halves' loads in flight before any store
-        const int i2 = i + kThreads;
-        const bool two = i2 < n16;
-        const uint4 k0 = kn[i];
-        const uint4 v0 = vn[i];
-        uint4 k1 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-        if (two) {
-          k1 = kn[i2];
-          v1 = vn[i2];
-        }
-        kd[i] = k0;
-        vd[i] = v0;
-        if (two) {
-          kd[i2] = k1;
-          vd[i2] = v1;
-        }
+    const size_t dst = ((size_t)blk * B + (size_t)(L % B)) * (size_t)a.row_b;
+    uint4* __restrict__ kd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst);
+    uint4* __restrict__ vd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst);
+    if (held) {
+      if (tid < n16) { kd[tid] = k0; vd[tid] = v0; }
+      if (tid + kThreads < n16) { kd[tid + kThreads] = k1; vd[tid + kThreads] = v1; }
+      if (tid + 2 * kThreads < n16) { kd[tid + 2 * kThreads] = k2; vd[tid + 2 * kThreads] = v2; }
+      if (tid + 3 * kThreads < n16) { kd[tid + 3 * kThreads] = k3; vd[tid + 3 * kThreads] = v3; }
+    } else {
+      for (int i = tid; i < n16; i += kThreads) {
+        const uint4 kv = kn[i];
+        const uint4 vv = vn[i];
+        kd[i] = kv;
+        vd[i] = vv;
       }
     }
   }
@@ -108,27 +126,22 @@ __global__ __launch_bounds__(kThreads) void shared_prepare_kernel(DecodeParams a
     for (int i = tid; i < a.Hq * head_dim; i += kThreads) o[i] = fill;
   }
   if (tid >= 64) return;
-  // Leading tokens shared with sequence s - 1: equal table entries, within
-  // the tokens both held before this step's append, in whole chunks.
-  int sh = 0;
-  if (s > 0 && La >= 0 && shared_attended_len(a, s - 1) >= 0) {
-    const int m = min(L, a.lens[s - 1]);
-    const int nb = (m + B - 1) / B;
-    const int32_t* t0 = a.tables + (size_t)(s - 1) * a.MB;
-    const int32_t* t1 = a.tables + (size_t)s * a.MB;
-    int e = nb;
-    for (int b0 = 0; b0 < nb; b0 += 64) {
+  // Leading equal entries: the first difference by a ballot, 64 entries a round.
+  int e = nb;
+  unsigned long long diff = __ballot(lane < nb && e0 != e1);
+  if (diff != 0ull) {
+    e = __builtin_ctzll(diff);
+  } else {
+    for (int b0 = 64; b0 < nb; b0 += 64) {
       const int b = b0 + lane;
-      const bool diff = b < nb && t0[b] != t1[b];
-      const unsigned long long mask = __ballot(diff);
-      if (mask != 0ull) {
-        e = b0 + __builtin_ctzll(mask);
+      diff = __ballot(b < nb && t0[b] != t1[b]);
+      if (diff != 0ull) {
+        e = b0 + __builtin_ctzll(diff);
         break;
       }
     }
-    sh = min(e * B, m) & ~(kChunk - 1);
   }
-  if (lane == 0) a.ws_share[s] = sh;
+  if (lane == 0) a.ws_share[s] = pair ? min(e * B, m) & ~(kChunk - 1) : 0;
 }
 
 // ------------------------------------------------------------ block scans
@@ -360,14 +373,22 @@ void decode_shared_kernel(DecodeParams a) {
     return;
   }
   const long long TC = (long long)NGR * uniform(T_cost);
-  auto last_group_at = [&](const int* pre, long long x) {  // last r with NGR * pre[r] <= x
+  // Last r in [0, R) with NGR * pre[r] <= x (pre nondecreasing, pre[0] = 0):
+  // each round the 64 lanes probe evenly spaced positions of the interval and
+  // a ballot keeps the piece between the last probe that holds and the next,
+  // so at most two rounds cover 2048 groups.
+  auto last_group_at = [&](const int* pre, long long x) {
     int ra = 0, rb = Ru;
     while (rb - ra > 1) {
-      const int mid = (ra + rb) >> 1;
-      if ((long long)NGR * uniform(pre[mid]) <= x) ra = mid;
-      else rb = mid;
+      const long long span = rb - ra;
+      const int pos = ra + (int)((span * lane) >> 6);
+      const unsigned long long m = __ballot((long long)NGR * pre[pos] <= x);
+      const int last = 63 - __builtin_clzll(m | 1ull);
+      const int nb = last == 63 ? rb : ra + (int)((span * (last + 1)) >> 6);
+      ra = ra + (int)((span * last) >> 6);
+      rb = nb;
     }
-    return ra;
+    return uniform(ra);
   };
   auto chunk_at = [&](long long x) -> long long {
     if (x >= TC) return T;
