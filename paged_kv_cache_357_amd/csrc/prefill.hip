@@ -67,7 +67,7 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
 // columns: scores K q^T, an online softmax per column with the mask limit
 // at the column's own position, and O^T += V^T P^T with the weights carried
 // as two bf16 parts.  A wave past its own last position only helps load.
-// Workgroup tiles are dealt last-first so the longest start first.
+// Workgroup tiles are numbered tile-major, last (longest) tiles first.
 
 // Headroom (base 2) a weight may reach before the prompt pass moves its
 // softmax reference.
@@ -95,9 +95,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(16))) char s_k[2][TILE];
   __shared__ __attribute__((aligned(16))) char s_v[2][TILE];
 
+  // Tile-major numbering, last (longest) tiles first: workgroups are dealt to
+  // the XCDs round robin, so each XCD gets every eighth (sequence, kv head)
+  // pair with all its tiles and runs them longest first.  (Numbering the
+  // tiles of a pair consecutively would give each XCD one tile index only
+  // whenever the tile count is a multiple of eight.)
   const int u = (int)blockIdx.x;
-  const int wgt = a.n_qt - 1 - u % a.n_qt;  // last tiles first
-  const int sg = u / a.n_qt;
+  const int n_sg = a.S * a.Hkv;
+  const int wgt = a.n_qt - 1 - u / n_sg;
+  const int sg = u - (u / n_sg) * n_sg;
   const int s = sg / a.Hkv;
   const int g = sg - s * a.Hkv;
   const int r0 = a.q_start[s];
