@@ -137,6 +137,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
   for (int k = 0; k < NT; ++k) p_col[k] = ok[k] ? L - n + tk[k] : -1;
   const int p_wave = t0 < n ? L - n + min(t0 + WT, n) - 1 : -1;       // last key of this wave
+  const int p_first = L - n + t0;                                     // last key of the wave's first column
   const int p_wg = L - n + min(wg_t0 + kWavesPerWG * WT, n) - 1;      // last key of the workgroup
   const int n_steps = p_wg / STEP + 1;
   const int32_t* trow = a.tables + (size_t)s * a.MB;
@@ -173,12 +174,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int lr = tid / LPR, lc = tid % LPR;
   const bool loader = lr < kChunk;
   bool bad = false;
+  // Table entry of each half of a step, read one step before the step's
+  // loads are issued: the scalar read then completes under a whole step of
+  // work (the barrier's wait covers it) instead of stalling the issue.
+  auto entry = [&](int c, int half) {
+    const int cs = c * STEP + half * kChunk;
+    return trow[(cs <= p_wg ? cs : 0) / B];
+  };
+  int nid[2] = {entry(0, 0), entry(0, 1)};
   auto load = [&](int c, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
+    int id[2] = {nid[0], nid[1]};
+    nid[0] = entry(c + 1, 0);
+    nid[1] = entry(c + 1, 1);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int cs = c * STEP + half * kChunk;
       const bool live = cs <= p_wg;
-      int blk = trow[(live ? cs : 0) / B];
+      int blk = id[half];
       if (blk < 0 || blk >= a.NB) {  // never dereferenced; the rows become NaN
         if (live) bad = true;
         blk = 0;
@@ -253,37 +265,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // more than kLazy (base 2), so weights stay below 2^kLazy and the
     // accumulator is rescaled rarely.  Any reference gives the same
     // softmax; only rounding depends on it, and it depends on the data
-    // alone, so results stay deterministic.
-    bf16x8 phi[NT], plo[NT];
+    // alone, so results stay deterministic.  The causal mask is applied only
+    // on steps that reach past the wave's first column's last key (columns
+    // past the chunk's end are never written, so they need no mask); one
+    // branch covers the rescale of every tile.
+    float x[NT][8], mx[NT];
+    auto scores_to_exponents = [&](auto masked) {
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        const int lim = p_col[k] - cs;
+        mx[k] = kNegBig;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = (i < 4 ? 0 : kChunk) + 4 * gl + (i & 3);
+          const float v = sc[k][i >> 2][i & 3] * a.scale_log2;
+          x[k][i] = (!decltype(masked)::value || key <= lim) ? v : -INFINITY;
+          mx[k] = fmaxf(mx[k], x[k][i]);
+        }
+      }
+    };
+    if (cs + STEP - 1 > p_first) scores_to_exponents(std::true_type{});
+    else scores_to_exponents(std::false_type{});
+    bool move[NT];
+    bool any_move = false;
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
-      const int lim = p_col[k] - cs;
-      float x[8];
-      float mx = kNegBig;
+      mx[k] = max_over_lane_groups(mx[k]);
+      move[k] = mx[k] > m_run[k] + kLazy;
+      any_move = any_move || move[k];
+    }
+    if (__any(any_move)) {  // rare: a tile whose columns keep their reference is scaled by exactly 1
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = (i < 4 ? 0 : kChunk) + 4 * gl + (i & 3);
-        x[i] = (key <= lim) ? sc[k][i >> 2][i & 3] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[i]);
-      }
-      mx = max_over_lane_groups(mx);
-      const bool move = mx > m_run[k] + kLazy;
-      if (__any(move)) {
-        const float m_new = move ? mx : m_run[k];
-        const float alpha = fast_exp2(m_run[k] - m_new);
-        m_run[k] = m_new;
+      for (int k = 0; k < NT; ++k) {
+        const float mn = move[k] ? mx[k] : m_run[k];
+        const float alpha = fast_exp2(m_run[k] - mn);
+        m_run[k] = mn;
         l_run[k] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < CW; ++dt) acc[k][dt] *= alpha;
       }
-      float pw[8];
-      float ps = 0.0f;
+    }
+    bf16x8 phi[NT], plo[NT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pw[i] = fast_exp2(x[i] - m_run[k]);
-        ps += pw[i];
-      }
-      l_run[k] += ps;
+    for (int k = 0; k < NT; ++k) {
+      float pw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pw[i] = fast_exp2(x[k][i] - m_run[k]);
+      l_run[k] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
       // P^T operand, high (truncated) and low (rounded rest) bf16 parts.
       uint32_t hb[8];
       float res[8];
