@@ -77,6 +77,10 @@ constexpr float kLazy = 8.0f;
 // feeds NT products, and the NT softmax chains interleave.
 constexpr int kTilesPerWave = kPrefillTilesPerWave;
 
+// Compute steps of 32 keys staged per LDS tile: the workgroup's four waves
+// meet at one barrier per tile.
+constexpr int kSubSteps = 2;
+
 // Two waves per SIMD: with that register budget the accumulators stay in
 // VGPRs (left to itself the compiler parks them in AGPRs and pays a copy
 // each way around every rescale).
@@ -89,9 +93,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int QT = 16 / G;            // tokens per 16-column tile
   constexpr int NT = kTilesPerWave;
   constexpr int WT = NT * QT;           // tokens per wave
-  constexpr int STEP = 2 * kChunk;      // keys per step: two 16-key halves
-  constexpr int TILE = STEP * ROW;      // bytes of one step of K (or V)
-  static_assert(kThreads >= kChunk * LPR, "one load per thread covers a half");
+  constexpr int STEP = 2 * kChunk;      // keys per compute step: two 16-key halves
+  constexpr int SUB = kSubSteps;        // compute steps per LDS tile (one barrier each tile)
+  constexpr int NQ = SUB * 2;           // 16-key quarters of a tile
+  constexpr int TILE = SUB * STEP * ROW;  // bytes of one tile of K (or V)
+  static_assert(kThreads >= kChunk * LPR, "one load per thread covers a quarter");
   __shared__ __attribute__((aligned(16))) char s_k[2][TILE];
   __shared__ __attribute__((aligned(16))) char s_v[2][TILE];
 
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int p_wave = t0 < n ? L - n + min(t0 + WT, n) - 1 : -1;       // last key of this wave
   const int p_first = L - n + t0;                                     // last key of the wave's first column
   const int p_wg = L - n + min(wg_t0 + kWavesPerWG * WT, n) - 1;      // last key of the workgroup
-  const int n_steps = p_wg / STEP + 1;
+  const int n_tiles = p_wg / (SUB * STEP) + 1;
   const int32_t* trow = a.tables + (size_t)s * a.MB;
   const uint32_t rs = (uint32_t)a.Hkv * ROW;
   const char* kbase = static_cast<const char*>(a.k) + (size_t)g * ROW;
@@ -167,71 +173,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     l_run[k] = 0.0f;
   }
 
-  // Step loads: for each 16-key half, thread tid moves 16 bytes (piece
-  // tid % LPR of row tid / LPR) of K and of V.  Halves past the last needed
-  // key go through zero-size resources (no data moves), so every step
-  // issues the same loads and each wait is exact.
-  const int lr = tid / LPR, lc = tid % LPR;
-  const bool loader = lr < kChunk;
-  bool bad = false;
-  // Table entry of each half of a step, read one step before the step's
-  // loads are issued: the scalar read then completes under a whole step of
+  // Tile loads: wave w moves quarter w of the tile (16 key rows of K and of
+  // V), so each wave builds one quarter's addresses; lane l takes row l / 4
+  // of the quarter and its 16-byte pieces l % 4 + 4 j, j < PPL.  Quarters
+  // past the last needed key go through zero-size resources (no data
+  // moves), so every tile issues the same loads and each wait is exact.
+  static_assert(NQ == kWavesPerWG, "one quarter of a tile per wave");
+  static_assert(LPR % 4 == 0 && 8 % CW == 0, "whole pieces per lane; V operand columns in whole pieces");
+  constexpr int PPL = LPR / 4;
+  const int lr = lane >> 2, lp = lane & 3;
+  int bad = 0;
+  // Table entry of this wave's quarter, read one tile before the quarter's
+  // loads are issued: the scalar read then completes under a whole tile of
   // work (the barrier's wait covers it) instead of stalling the issue.
-  auto entry = [&](int c, int half) {
-    const int cs = c * STEP + half * kChunk;
+  auto entry = [&](int c) {
+    const int cs = c * SUB * STEP + wave * kChunk;
     return trow[(cs <= p_wg ? cs : 0) / B];
   };
-  int nid[2] = {entry(0, 0), entry(0, 1)};
-  auto load = [&](int c, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
-    int id[2] = {nid[0], nid[1]};
-    nid[0] = entry(c + 1, 0);
-    nid[1] = entry(c + 1, 1);
+  int nid = entry(0);
+  auto load = [&](int c, u32x4 (&kr)[PPL], u32x4 (&vr)[PPL]) {
+    int blk = nid;
+    nid = entry(c + 1);
+    const int cs = c * SUB * STEP + wave * kChunk;
+    const bool live = cs <= p_wg;
+    const bool inpool = (unsigned)blk < (unsigned)a.NB;  // an id outside the pool is never dereferenced
+    bad |= (live && !inpool) ? 1 : 0;                     // its rows become NaN
+    blk = inpool ? blk : 0;
+    const size_t cbase = ((size_t)blk * B + (size_t)(cs % B)) * rs;
+    const int lim = min(kChunk - 1, p_wg - cs);  // rows past the last needed key read as zero
+    const uint32_t nbytes = live ? (uint32_t)lim * rs + ROW : 0u;
+    const __amdgpu_buffer_rsrc_t kres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + cbase), 0, (int)nbytes, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t vres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + cbase), 0, (int)nbytes, kBufferConfig);
+    const int off = (int)((uint32_t)lr * rs) + lp * 16;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int cs = c * STEP + half * kChunk;
-      const bool live = cs <= p_wg;
-      int blk = id[half];
-      if (blk < 0 || blk >= a.NB) {  // never dereferenced; the rows become NaN
-        if (live) bad = true;
-        blk = 0;
-      }
-      const size_t cbase = ((size_t)blk * B + (size_t)(cs % B)) * rs;
-      const int lim = min(kChunk - 1, p_wg - cs);  // rows past the last needed key read as zero
-      const uint32_t nbytes = live ? (uint32_t)lim * rs + ROW : 0u;
-      const __amdgpu_buffer_rsrc_t kres =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + cbase), 0, (int)nbytes, kBufferConfig);
-      const __amdgpu_buffer_rsrc_t vres =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + cbase), 0, (int)nbytes, kBufferConfig);
-      const int off = loader ? (int)((uint32_t)lr * rs) + lc * 16 : (int)nbytes;  // idle threads load nothing
-      kr[half] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, off, 0, 0));
-      vr[half] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0));
+    for (int jj = 0; jj < PPL; ++jj) {
+      kr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, off + 64 * jj, 0, 0));
+      vr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off + 64 * jj, 0, 0));
     }
   };
   // V goes into LDS already in operand order: for output tile dt and lane
   // (gl, cl) the eight bf16 of k slots 0..7 (keys 4 gl + 0..3, 16 + 4 gl +
   // 0..3) at column d = CW cl + dt sit in 16 consecutive bytes, so each wave
   // reads its V operand with one 16-byte read per tile and no shuffling.
-  // This thread holds d = 8 lc .. 8 lc + 7 of key row lr of each half.
-  int vt_off[8];
+  // Element i of piece p = lp + 4 jj (column d = 8 p + i) of key row lr of a
+  // 16-key half lands at byte ((dt * 64 + (lr / 4) * 16 + cl) * 8 + lr % 4) * 2
+  // with cl = d / CW, dt = d % CW: a lane part plus a constant.
+  const int vlane = (((lr >> 2) * 16 + (8 / CW) * lp) * 8 + (lr & 3)) * 2;
+  const int krow = wave * kChunk + lr;  // row of the tile this lane stores
+  auto store = [&](int buf, const u32x4 (&kr)[PPL], const u32x4 (&vr)[PPL]) {
+    char* vq = s_v[buf] + (wave / 2) * (STEP * ROW) + (wave % 2) * 8 + vlane;  // compute step, half of it
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int d = 8 * lc + i;
-    const int vcl = d / CW, vdt = d % CW;
-    vt_off[i] = ((vdt * 64 + (lr / 4) * 16 + vcl) * 8 + (lr % 4)) * 2;  // + 8 bytes for the second half
-  }
-  auto store = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
-    if (!loader) return;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int r = half * kChunk + lr;
-      // K: piece lc of row r at (lc ^ (r mod LPR)), so the operand reads
-      // (16 rows at one piece) fall in distinct banks.
-      *reinterpret_cast<u32x4*>(s_k[buf] + r * ROW + ((lc ^ (r % LPR)) * 16)) = kr[half];
+    for (int jj = 0; jj < PPL; ++jj) {
+      // K: piece p of row r at (p ^ (r mod LPR)), so the operand reads (16
+      // rows at one piece) fall in distinct banks.
+      const int pc = (lp + 4 * jj) ^ (krow % LPR);
+      *reinterpret_cast<u32x4*>(s_k[buf] + krow * ROW + pc * 16) = kr[jj];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t wd = vr[half][i / 2];
+        const int vcon = ((i % CW) * 64 + (8 / CW) * 4 * jj + i / CW) * 16;
+        const uint32_t wd = vr[jj][i / 2];
         const unsigned short v16 = (unsigned short)((i % 2 == 0) ? (wd & 0xffffu) : (wd >> 16));
-        *reinterpret_cast<unsigned short*>(s_v[buf] + vt_off[i] + half * 8) = v16;
+        *reinterpret_cast<unsigned short*>(vq + vcon) = v16;
       }
     }
   };
@@ -243,8 +247,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // tile; its k index order is the same for both operands (k slot 8 gl + i
   // is key 4 gl + i for i < 4, 16 + 4 gl + i - 4 after), so the lane's eight
   // weights are its B operand as they stand.
-  auto compute = [&](int c, int buf) {
+  auto compute = [&](int c, int buf, int sub) {
     const int cs = c * STEP;
+    const char* ktile = s_k[buf] + sub * (STEP * ROW);
+    const char* vtile = s_v[buf] + sub * (STEP * ROW);
     f32x4 sc[NT][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) {
         const int pc = (gl + 4 * j) ^ (r % LPR);
-        const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k[buf] + r * ROW + pc * 16));
+        const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + r * ROW + pc * 16));
 #pragma unroll
         for (int k = 0; k < NT; ++k) sc[k][half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[k][j], sc[k][half], 0, 0, 0);
       }
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int dt = 0; dt < CW; ++dt) {
       const bf16x8 vt =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_v[buf] + (dt * 64 + gl * 16 + cl) * 16));
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vtile + (dt * 64 + gl * 16 + cl) * 16));
 #pragma unroll
       for (int k = 0; k < NT; ++k) {
         acc[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[k], acc[k][dt], 0, 0, 0);
@@ -338,18 +344,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  // Step loop: the next step is loaded into registers while step c is
-  // computed from one LDS buffer, then stored into the other; one barrier
-  // per step.  (Deeper prefetch measured no faster: the pass is bound by the
-  // wave's own instruction chain, not by load latency.)
-  u32x4 kr[2], vr[2];
+  // Tile loop: the next tile (SUB compute steps of K and V) is loaded into
+  // registers while tile c is computed from one LDS buffer, then stored into
+  // the other; one barrier per tile.  (Deeper prefetch measured no faster:
+  // the pass is bound by the wave's own instruction chain, not by load
+  // latency.)
+  u32x4 kr[PPL], vr[PPL];
   load(0, kr, vr);
   store(0, kr, vr);
   __syncthreads();
-  for (int c = 0; c < n_steps; ++c) {
-    if (c + 1 < n_steps) load(c + 1, kr, vr);
-    if (c * STEP <= p_wave) compute(c, c & 1);
-    if (c + 1 < n_steps) store((c + 1) & 1, kr, vr);
+  for (int c = 0; c < n_tiles; ++c) {
+    if (c + 1 < n_tiles) load(c + 1, kr, vr);
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int cstep = c * SUB + sub;
+      if (cstep * STEP <= p_wave) compute(cstep, c & 1, sub);
+    }
+    if (c + 1 < n_tiles) store((c + 1) & 1, kr, vr);
     __syncthreads();
   }
   bad = __syncthreads_or(bad);
