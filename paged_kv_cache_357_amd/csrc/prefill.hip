@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // past the last needed key go through zero-size resources (no data
   // moves), so every tile issues the same loads and each wait is exact.
   static_assert(NQ == kWavesPerWG, "one quarter of a tile per wave");
-  static_assert(LPR % 4 == 0 && 8 % CW == 0, "whole pieces per lane; V operand columns in whole pieces");
+  static_assert(LPR % 4 == 0, "whole pieces per lane");
   constexpr int PPL = LPR / 4;
   const int lr = lane >> 2, lp = lane & 3;
   int bad = 0;
@@ -213,31 +213,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       vr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off + 64 * jj, 0, 0));
     }
   };
-  // V goes into LDS already in operand order: for output tile dt and lane
-  // (gl, cl) the eight bf16 of k slots 0..7 (keys 4 gl + 0..3, 16 + 4 gl +
-  // 0..3) at column d = CW cl + dt sit in 16 consecutive bytes, so each wave
-  // reads its V operand with one 16-byte read per tile and no shuffling.
-  // Element i of piece p = lp + 4 jj (column d = 8 p + i) of key row lr of a
-  // 16-key half lands at byte ((dt * 64 + (lr / 4) * 16 + cl) * 8 + lr % 4) * 2
-  // with cl = d / CW, dt = d % CW: a lane part plus a constant.
-  const int vlane = (((lr >> 2) * 16 + (8 / CW) * lp) * 8 + (lr & 3)) * 2;
+  // K and V go into LDS as they are laid out in the pool, one 256-byte row
+  // (D = 128) per key, with 16-byte piece p of row r stored at (p ^ (r mod
+  // LPR)): the K operand reads (16 rows at one piece) and the transposing V
+  // reads (four rows at two pieces per lane group) fall in distinct banks.
   const int krow = wave * kChunk + lr;  // row of the tile this lane stores
   auto store = [&](int buf, const u32x4 (&kr)[PPL], const u32x4 (&vr)[PPL]) {
-    char* vq = s_v[buf] + (wave / 2) * (STEP * ROW) + (wave % 2) * 8 + vlane;  // compute step, half of it
 #pragma unroll
     for (int jj = 0; jj < PPL; ++jj) {
-      // K: piece p of row r at (p ^ (r mod LPR)), so the operand reads (16
-      // rows at one piece) fall in distinct banks.
       const int pc = (lp + 4 * jj) ^ (krow % LPR);
       *reinterpret_cast<u32x4*>(s_k[buf] + krow * ROW + pc * 16) = kr[jj];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int vcon = ((i % CW) * 64 + (8 / CW) * 4 * jj + i / CW) * 16;
-        const uint32_t wd = vr[jj][i / 2];
-        const unsigned short v16 = (unsigned short)((i % 2 == 0) ? (wd & 0xffffu) : (wd >> 16));
-        *reinterpret_cast<unsigned short*>(vq + vcon) = v16;
-      }
+      *reinterpret_cast<u32x4*>(s_v[buf] + krow * ROW + pc * 16) = vr[jj];
     }
+  };
+  // V operand of output tile dt (columns d = 16 dt + i, i < 16) by two
+  // transposing reads (ds_read_b64_tr_b16): within a group of 16 lanes, lane
+  // i receives as element j the 16-bit element i % 4 of the 8 bytes that
+  // lane 4 j + i / 4 addresses (measured lane layout on gfx950).  Lane
+  // 4 j + q of group gl addresses row 4 gl + j (16 + 4 gl + j for the second
+  // read), columns 16 dt + 4 q .. + 3, so lane (gl, cl) gets column
+  // 16 dt + cl of keys 4 gl + 0..3 and 16 + 4 gl + 0..3: the k slots of its
+  // weights.
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int tr_row = 4 * gl + (cl >> 2);
+  const int tr_q = cl & 3;
+  auto v_operand = [&](const char* vtile, int dt) -> bf16x8 {
+    u32x2 h[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int r = half * kChunk + tr_row;
+      const int piece = (2 * dt + (tr_q >> 1)) ^ (r % LPR);
+      const char* src = vtile + r * ROW + piece * 16 + (tr_q & 1) * 8;
+      h[half] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src));
+    }
+    return __builtin_bit_cast(bf16x8, u32x4{h[0][0], h[0][1], h[1][0], h[1][1]});
   };
 
   // One 32-key step for this wave's NT tiles of 16 columns.  Lane (gl, cl)
@@ -334,8 +344,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 #pragma unroll
     for (int dt = 0; dt < CW; ++dt) {
-      const bf16x8 vt =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vtile + (dt * 64 + gl * 16 + cl) * 16));
+      const bf16x8 vt = v_operand(vtile, dt);
 #pragma unroll
       for (int k = 0; k < NT; ++k) {
         acc[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[k], acc[k][dt], 0, 0, 0);
@@ -365,23 +374,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   bad = __syncthreads_or(bad);
 
-  // Lane (gl, cl) holds output columns CW * (4 gl + r) + dt of its row; the
-  // four lane groups share the running reference, their sums add.
-  const int col0 = 4 * CW * gl;
+  // Lane (gl, cl) holds output columns 16 dt + 4 gl + r of its row; the four
+  // lane groups share the running reference, their sums add.
+  const int col0 = 4 * gl;
   const float nan = __builtin_nanf("");
 #pragma unroll
   for (int k = 0; k < NT; ++k) {
     float lt = l_run[k] + __shfl_xor(l_run[k], 16);
     lt += __shfl_xor(lt, 32);
     if (!ok[k]) continue;
-    float4* dst = reinterpret_cast<float4*>(orow[k] + col0);
 #pragma unroll
-    for (int e = 0; e < 4 * CW; e += 4) {
-      float v4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v4[i] = acc[k][(e + i) % CW][(e + i) / CW];
-      dst[e / 4] = bad ? make_float4(nan, nan, nan, nan)
-                       : make_float4(v4[0] / lt, v4[1] / lt, v4[2] / lt, v4[3] / lt);
+    for (int dt = 0; dt < CW; ++dt) {
+      const f32x4 v4 = acc[k][dt];
+      *reinterpret_cast<float4*>(orow[k] + 16 * dt + col0) =
+          bad ? make_float4(nan, nan, nan, nan) : make_float4(v4[0] / lt, v4[1] / lt, v4[2] / lt, v4[3] / lt);
     }
   }
 }
