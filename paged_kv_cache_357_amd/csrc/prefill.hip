@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int STEP = 2 * kChunk;      // keys per compute step: two 16-key halves
   constexpr int SUB = kSubSteps;        // compute steps per LDS tile (one barrier each tile)
   constexpr int NQ = SUB * 2;           // 16-key quarters of a tile
-  constexpr int TILE = SUB * STEP * ROW;  // bytes of one tile of K (or V)
+  constexpr int ROWP = ROW + 16;        // LDS row stride: a 16-byte pad staggers the banks of successive rows
+  constexpr int TILE = SUB * STEP * ROWP;  // bytes of one tile of K (or V)
   static_assert(kThreads >= kChunk * LPR, "one load per thread covers a quarter");
   __shared__ __attribute__((aligned(16))) char s_k[2][TILE];
   __shared__ __attribute__((aligned(16))) char s_v[2][TILE];
@@ -213,17 +214,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       vr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off + 64 * jj, 0, 0));
     }
   };
-  // K and V go into LDS as they are laid out in the pool, one 256-byte row
-  // (D = 128) per key, with 16-byte piece p of row r stored at (p ^ (r mod
-  // LPR)): the K operand reads (16 rows at one piece) and the transposing V
-  // reads (four rows at two pieces per lane group) fall in distinct banks.
+  // K and V go into LDS as they are laid out in the pool, one row per key
+  // at a stride of ROWP bytes: the pad shifts successive rows by four banks,
+  // so the K operand reads (16 rows at one piece) and the transposing V reads
+  // (four rows at two pieces per lane group) spread over the banks, and
+  // every operand address is a lane base plus a constant.
   const int krow = wave * kChunk + lr;  // row of the tile this lane stores
   auto store = [&](int buf, const u32x4 (&kr)[PPL], const u32x4 (&vr)[PPL]) {
 #pragma unroll
     for (int jj = 0; jj < PPL; ++jj) {
-      const int pc = (lp + 4 * jj) ^ (krow % LPR);
-      *reinterpret_cast<u32x4*>(s_k[buf] + krow * ROW + pc * 16) = kr[jj];
-      *reinterpret_cast<u32x4*>(s_v[buf] + krow * ROW + pc * 16) = vr[jj];
+      const int off = krow * ROWP + (lp + 4 * jj) * 16;
+      *reinterpret_cast<u32x4*>(s_k[buf] + off) = kr[jj];
+      *reinterpret_cast<u32x4*>(s_v[buf] + off) = vr[jj];
     }
   };
   // V operand of output tile dt (columns d = 16 dt + i, i < 16) by two
@@ -242,9 +244,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     u32x2 h[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int r = half * kChunk + tr_row;
-      const int piece = (2 * dt + (tr_q >> 1)) ^ (r % LPR);
-      const char* src = vtile + r * ROW + piece * 16 + (tr_q & 1) * 8;
+      const char* src = vtile + (half * kChunk + tr_row) * ROWP + 32 * dt + 8 * tr_q;
       h[half] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src));
     }
     return __builtin_bit_cast(bf16x8, u32x4{h[0][0], h[0][1], h[1][0], h[1][1]});
@@ -259,8 +259,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // weights are its B operand as they stand.
   auto compute = [&](int c, int buf, int sub) {
     const int cs = c * STEP;
-    const char* ktile = s_k[buf] + sub * (STEP * ROW);
-    const char* vtile = s_v[buf] + sub * (STEP * ROW);
+    const char* ktile = s_k[buf] + sub * (STEP * ROWP);
+    const char* vtile = s_v[buf] + sub * (STEP * ROWP);
     f32x4 sc[NT][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -269,8 +269,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int r = half * kChunk + cl;
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) {
-        const int pc = (gl + 4 * j) ^ (r % LPR);
-        const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + r * ROW + pc * 16));
+        const bf16x8 kop =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + r * ROWP + (gl + 4 * j) * 16));
 #pragma unroll
         for (int k = 0; k < NT; ++k) sc[k][half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[k][j], sc[k][half], 0, 0, 0);
       }
