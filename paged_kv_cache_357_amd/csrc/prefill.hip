@@ -96,11 +96,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int STEP = 2 * kChunk;      // keys per compute step: two 16-key halves
   constexpr int SUB = kSubSteps;        // compute steps per LDS tile (one barrier each tile)
   constexpr int NQ = SUB * 2;           // 16-key quarters of a tile
-  constexpr int ROWP = ROW + 16;        // LDS row stride: a 16-byte pad staggers the banks of successive rows
-  constexpr int TILE = SUB * STEP * ROWP;  // bytes of one tile of K (or V)
+  constexpr int KROW = ROW + 16;        // LDS row strides of K and V (padding against bank conflicts)
+  constexpr int VROW = ROW + 32;
   static_assert(kThreads >= kChunk * LPR, "one load per thread covers a quarter");
-  __shared__ __attribute__((aligned(16))) char s_k[2][TILE];
-  __shared__ __attribute__((aligned(16))) char s_v[2][TILE];
+  __shared__ __attribute__((aligned(16))) char s_k[2][SUB * STEP * KROW];
+  __shared__ __attribute__((aligned(16))) char s_v[2][SUB * STEP * VROW];
 
   // Tile-major numbering, last (longest) tiles first: workgroups are dealt to
   // the XCDs round robin, so each XCD gets every eighth (sequence, kv head)
@@ -214,18 +214,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       vr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off + 64 * jj, 0, 0));
     }
   };
-  // K and V go into LDS as they are laid out in the pool, one row per key
-  // at a stride of ROWP bytes: the pad shifts successive rows by four banks,
-  // so the K operand reads (16 rows at one piece) and the transposing V reads
-  // (four rows at two pieces per lane group) spread over the banks, and
-  // every operand address is a lane base plus a constant.
+  // K and V go into LDS as they are laid out in the pool, one row per key,
+  // padded so that every operand address is a lane base plus a constant and
+  // the operand reads spread over the banks: K rows KROW = ROW + 16 bytes
+  // apart put the K operand reads (16 rows at one 16-byte piece) in 16
+  // different 16-byte bank slots; V rows VROW = ROW + 32 bytes apart put each
+  // lane group's transposing read (four rows at 32 bytes each) in four
+  // different 32-byte slots.
   const int krow = wave * kChunk + lr;  // row of the tile this lane stores
   auto store = [&](int buf, const u32x4 (&kr)[PPL], const u32x4 (&vr)[PPL]) {
 #pragma unroll
     for (int jj = 0; jj < PPL; ++jj) {
-      const int off = krow * ROWP + (lp + 4 * jj) * 16;
-      *reinterpret_cast<u32x4*>(s_k[buf] + off) = kr[jj];
-      *reinterpret_cast<u32x4*>(s_v[buf] + off) = vr[jj];
+      *reinterpret_cast<u32x4*>(s_k[buf] + krow * KROW + (lp + 4 * jj) * 16) = kr[jj];
+      *reinterpret_cast<u32x4*>(s_v[buf] + krow * VROW + (lp + 4 * jj) * 16) = vr[jj];
     }
   };
   // V operand of output tile dt (columns d = 16 dt + i, i < 16) by two
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     u32x2 h[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const char* src = vtile + (half * kChunk + tr_row) * ROWP + 32 * dt + 8 * tr_q;
+      const char* src = vtile + (half * kChunk + tr_row) * VROW + 32 * dt + 8 * tr_q;
       h[half] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src));
     }
     return __builtin_bit_cast(bf16x8, u32x4{h[0][0], h[0][1], h[1][0], h[1][1]});
@@ -259,8 +260,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // weights are its B operand as they stand.
   auto compute = [&](int c, int buf, int sub) {
     const int cs = c * STEP;
-    const char* ktile = s_k[buf] + sub * (STEP * ROWP);
-    const char* vtile = s_v[buf] + sub * (STEP * ROWP);
+    const char* ktile = s_k[buf] + sub * (STEP * KROW);
+    const char* vtile = s_v[buf] + sub * (STEP * VROW);
     f32x4 sc[NT][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) {
         const bf16x8 kop =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + r * ROWP + (gl + 4 * j) * 16));
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + r * KROW + (gl + 4 * j) * 16));
 #pragma unroll
         for (int k = 0; k < NT; ++k) sc[k][half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[k][j], sc[k][half], 0, 0, 0);
       }
