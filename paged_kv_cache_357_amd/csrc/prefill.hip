@@ -95,7 +95,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int WT = NT * QT;           // tokens per wave
   constexpr int STEP = 2 * kChunk;      // keys per compute step: two 16-key halves
   constexpr int SUB = kSubSteps;        // compute steps per LDS tile (one barrier each tile)
-  constexpr int NQ = SUB * 2;           // 16-key quarters of a tile
   constexpr int KROW = ROW + 16;        // LDS row strides of K and V (padding against bank conflicts)
   constexpr int VROW = ROW + 32;
   static_assert(kThreads >= kChunk * LPR, "one load per thread covers a quarter");
@@ -174,34 +173,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     l_run[k] = 0.0f;
   }
 
-  // Tile loads: wave w moves quarter w of the tile (16 key rows of K and of
-  // V), so each wave builds one quarter's addresses; lane l takes row l / 4
-  // of the quarter and its 16-byte pieces l % 4 + 4 j, j < PPL.  Quarters
-  // past the last needed key go through zero-size resources (no data
-  // moves), so every tile issues the same loads and each wait is exact.
-  static_assert(NQ == kWavesPerWG, "one quarter of a tile per wave");
-  static_assert(LPR % 4 == 0, "whole pieces per lane");
-  constexpr int PPL = LPR / 4;
-  const int lr = lane >> 2, lp = lane & 3;
+  // Tile loads: wave w moves rows w RPW .. w RPW + RPW - 1 of the tile (K
+  // and V), so each wave builds the addresses of one piece of one block;
+  // lane l takes row l / LPW of them and its 16-byte pieces l % LPW + LPW j,
+  // j < PPL.  Rows past the last needed key go through zero-size resources
+  // (no data moves), so every tile issues the same loads and each wait is
+  // exact.
+  constexpr int RPW = SUB * STEP / kWavesPerWG;  // rows per wave: 16 / RPW of them share a 16-key chunk
+  constexpr int LPW = 64 / RPW;                  // lanes per row
+  static_assert(kChunk % RPW == 0 && LPR % LPW == 0, "a wave's rows lie in one block; whole pieces per lane");
+  constexpr int PPL = LPR / LPW;
+  const int lr = lane / LPW, lp = lane % LPW;
   int bad = 0;
-  // Table entry of this wave's quarter, read one tile before the quarter's
-  // loads are issued: the scalar read then completes under a whole tile of
-  // work (the barrier's wait covers it) instead of stalling the issue.
+  // Table entry of this wave's rows, read one tile before their loads are
+  // issued: the scalar read then completes under a whole tile of work (the
+  // barrier's wait covers it) instead of stalling the issue.
   auto entry = [&](int c) {
-    const int cs = c * SUB * STEP + wave * kChunk;
+    const int cs = c * SUB * STEP + wave * RPW;
     return trow[(cs <= p_wg ? cs : 0) / B];
   };
   int nid = entry(0);
   auto load = [&](int c, u32x4 (&kr)[PPL], u32x4 (&vr)[PPL]) {
     int blk = nid;
     nid = entry(c + 1);
-    const int cs = c * SUB * STEP + wave * kChunk;
+    const int cs = c * SUB * STEP + wave * RPW;
     const bool live = cs <= p_wg;
     const bool inpool = (unsigned)blk < (unsigned)a.NB;  // an id outside the pool is never dereferenced
     bad |= (live && !inpool) ? 1 : 0;                     // its rows become NaN
     blk = inpool ? blk : 0;
     const size_t cbase = ((size_t)blk * B + (size_t)(cs % B)) * rs;
-    const int lim = min(kChunk - 1, p_wg - cs);  // rows past the last needed key read as zero
+    const int lim = min(RPW - 1, p_wg - cs);  // rows past the last needed key read as zero
     const uint32_t nbytes = live ? (uint32_t)lim * rs + ROW : 0u;
     const __amdgpu_buffer_rsrc_t kres =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + cbase), 0, (int)nbytes, kBufferConfig);
@@ -210,8 +211,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int off = (int)((uint32_t)lr * rs) + lp * 16;
 #pragma unroll
     for (int jj = 0; jj < PPL; ++jj) {
-      kr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, off + 64 * jj, 0, 0));
-      vr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off + 64 * jj, 0, 0));
+      kr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, off + 16 * LPW * jj, 0, 0));
+      vr[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, off + 16 * LPW * jj, 0, 0));
     }
   };
   // K and V go into LDS as they are laid out in the pool, one row per key,
@@ -221,12 +222,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // different 16-byte bank slots; V rows VROW = ROW + 32 bytes apart put each
   // lane group's transposing read (four rows at 32 bytes each) in four
   // different 32-byte slots.
-  const int krow = wave * kChunk + lr;  // row of the tile this lane stores
+  const int krow = wave * RPW + lr;  // row of the tile this lane stores
   auto store = [&](int buf, const u32x4 (&kr)[PPL], const u32x4 (&vr)[PPL]) {
 #pragma unroll
     for (int jj = 0; jj < PPL; ++jj) {
-      *reinterpret_cast<u32x4*>(s_k[buf] + krow * KROW + (lp + 4 * jj) * 16) = kr[jj];
-      *reinterpret_cast<u32x4*>(s_v[buf] + krow * VROW + (lp + 4 * jj) * 16) = vr[jj];
+      *reinterpret_cast<u32x4*>(s_k[buf] + krow * KROW + (lp + LPW * jj) * 16) = kr[jj];
+      *reinterpret_cast<u32x4*>(s_v[buf] + krow * VROW + (lp + LPW * jj) * 16) = vr[jj];
     }
   };
   // V operand of output tile dt (columns d = 16 dt + i, i < 16) by two
