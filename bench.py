@@ -370,14 +370,24 @@ def write_traces(args):
         with open(p, newline="") as f:
             rows += list(csv.DictReader(f))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    cmd = profile_command(args)
-    lines = [f"# rocprofv3 kernel trace of the {args.workload} step (call {args.call}), MI355X",
+    if args.prefill_only:
+        cmd = f"python bench.py --prefill-only --steps {args.steps}"
+        what = "prompt pass at the Llama-7B shape (4 sequences, 1024-token chunks over 2048-token contexts)"
+        rerun = f"python bench.py --prefill-only --steps {args.steps} --write-traces gpurun_out/trace"
+        note = [f"# The run holds 2 warm-up calls and {args.steps} timed calls, each after a 1 GiB flush (fill kernel)."]
+        out = os.path.join(PROFILES, "kernel_trace_prefill_llama7b-shape.md")
+    else:
+        cmd = profile_command(args)
+        what = f"{args.workload} step (call {args.call})"
+        rerun = f"python bench.py --workload {args.workload} --call {args.call} --write-traces gpurun_out/trace"
+        note = ["# The run holds 1 warm-up and 3 timed steps, then the same number of stage-1 repetitions,",
+                "# each after a 1 GiB flush (fill kernel), and 3 steps back to back."]
+        out = os.path.join(PROFILES, f"kernel_trace_{args.workload}_{args.call}.md")
+    lines = [f"# rocprofv3 kernel trace of the {what}, MI355X",
              "#", "#   cd /tmp && export TMPDIR=/tmp && cd <repository root> &&",
              f"#   timeout -k 10 300 rocprofv3 --kernel-trace --stats -d gpurun_out/trace -o run "
              f"--output-format csv -- {cmd}",
-             f"#   python bench.py --workload {args.workload} --call {args.call} --write-traces gpurun_out/trace",
-             "#", "# The run holds 1 warm-up and 3 timed steps, then the same number of stage-1 repetitions,",
-             "# each after a 1 GiB flush (fill kernel), and 3 steps back to back.", "",
+             f"#   {rerun}", "#", *note, "",
              "| kernel | calls | mean us | min us | max us |", "|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
@@ -385,7 +395,6 @@ def write_traces(args):
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
     text = "\n".join(lines) + "\n"
-    out = os.path.join(PROFILES, f"kernel_trace_{args.workload}_{args.call}.md")
     with open(out, "w") as f:
         f.write(text)
     print(text)
