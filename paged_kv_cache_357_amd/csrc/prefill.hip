@@ -34,19 +34,6 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ u32x4 make_u32x4(const uint4& t) { return u32x4{t.x, t.y, t.z, t.w}; }
 
-// Largest x over lanes l, l ^ 16, l ^ 32 and l ^ 48, without an LDS round
-// trip: with both operands x, v_permlane16_swap leaves each lane its own x
-// in one result and lane l ^ 16's in the other (rows of 16 lanes swap in
-// pairs), and v_permlane32_swap does the same for lane l ^ 32 (measured lane
-// layout on gfx950).  The maximum is exact, so the result equals the shuffle
-// form bit for bit.
-__device__ __forceinline__ float max_over_lane_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 // Two floats rounded to bf16 (round to nearest even), a in the low half.
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -57,47 +44,47 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
 //
 // Causal attention of a chunk of new query tokens over their sequence's
 // cache (the chunk's own K and V already written): the token at position p
-// attends to positions 0 .. p.  A wave takes a tile of 16 query columns,
-// the (token, head) pairs of QT = 16 / G consecutive tokens and the G query
-// heads of kv head g; a workgroup takes four consecutive tiles of one
-// (sequence, kv head).  The workgroup streams the sequence's 16-token chunks
-// from position 0 to its last token's position: all 256 threads load a
-// chunk's K and V rows once into a double-buffered LDS tile (one barrier
-// per chunk), and each wave runs the decode step's matrix-core math on its
-// columns: scores K q^T, an online softmax per column with the mask limit
-// at the column's own position, and O^T += V^T P^T with the weights carried
-// as two bf16 parts.  A wave past its own last position only helps load.
-// Workgroup tiles are numbered tile-major, last (longest) tiles first.
+// attends to positions 0 .. p.  A wave takes 32 query columns, the (token,
+// head) pairs of 32 / G consecutive tokens and the G query heads of kv head
+// g; a workgroup takes four such waves of one (sequence, kv head).  The
+// workgroup streams the sequence's keys from position 0 to its last token's
+// position in tiles of 64: all 256 threads load a tile's K and V rows once
+// into a double-buffered LDS tile (one barrier per tile), and each wave runs
+// 32-key steps of matrix-core math on its columns: scores K q^T
+// (v_mfma_f32_32x32x16_bf16), an online softmax per column with the mask
+// limit at the column's own position, and O^T += V^T P^T with the weights
+// carried as two bf16 parts.  A wave past its own last position only helps
+// load.  Workgroup tiles are numbered tile-major, last (longest) tiles first.
+//
+// Lane layout of v_mfma_f32_32x32x16_bf16 (measured on gfx950 with a
+// one-wave probe): lane l holds row l % 32 of the A operand at k = 8 (l / 32)
+// + t and column l % 32 of the B operand at the same k, t < 8; result element
+// r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
 
 // Headroom (base 2) a weight may reach before the prompt pass moves its
 // softmax reference.
 constexpr float kLazy = 8.0f;
 
-// Query tiles per wave: each K operand read and each assembled V operand
-// feeds NT products, and the NT softmax chains interleave.
-constexpr int kTilesPerWave = kPrefillTilesPerWave;
-
 // Compute steps of 32 keys staged per LDS tile: the workgroup's four waves
 // meet at one barrier per tile.
 constexpr int kSubSteps = 2;
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 // Two waves per SIMD: with that register budget the accumulators stay in
-// VGPRs (left to itself the compiler parks them in AGPRs and pays a copy
-// each way around every rescale).
+// VGPRs.
 template <int D, int B, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillParams a) {
+  static_assert(kPrefillTilesPerWave * 16 == 32, "a wave takes 32 query columns");
   constexpr int ROW = D * 2;            // bytes of one token row of one kv head
   constexpr int LPR = ROW / 16;         // 16-byte pieces per row
-  constexpr int KSTEPS = D / 32;
-  constexpr int CW = D / 16;            // bf16 per lane of a V row = output tiles
-  constexpr int QT = 16 / G;            // tokens per 16-column tile
-  constexpr int NT = kTilesPerWave;
-  constexpr int WT = NT * QT;           // tokens per wave
-  constexpr int STEP = 2 * kChunk;      // keys per compute step: two 16-key halves
+  constexpr int KS = D / 16;            // score products per step (16 of d each)
+  constexpr int DB = D / 32;            // output blocks of 32 columns of d
+  constexpr int WT = 32 / G;            // tokens per wave
+  constexpr int STEP = 32;              // keys per compute step
   constexpr int SUB = kSubSteps;        // compute steps per LDS tile (one barrier each tile)
   constexpr int KROW = ROW + 16;        // LDS row strides of K and V (padding against bank conflicts)
-  constexpr int VROW = ROW + 32;
-  static_assert(kThreads >= kChunk * LPR, "one load per thread covers a quarter");
+  constexpr int VROW = ROW + 64;
   __shared__ __attribute__((aligned(16))) char s_k[2][SUB * STEP * KROW];
   __shared__ __attribute__((aligned(16))) char s_v[2][SUB * STEP * VROW];
 
@@ -120,28 +107,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int wg_t0 = wgt * kWavesPerWG * WT;
   if (wg_t0 >= n) return;  // uniform over the workgroup
   const int L = a.lens[s];
-  const int cl = lane & 15, gl = lane >> 4;
+  const int col = lane & 31, hl = lane >> 5;  // this lane's query column; which half of the k range it holds
   const int t0 = wg_t0 + wave * WT;
-  const int h = cl % G;                    // this lane's column in tile k: token t0 + k QT + cl / G, head h
-  int tk[NT];
-  bool ok[NT];
-  float* orow[NT];
-#pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    tk[k] = t0 + k * QT + cl / G;
-    ok[k] = tk[k] < n;
-    orow[k] = a.out + ((size_t)(r0 + tk[k]) * a.Hq + (size_t)g * G + h) * D;
-  }
-  if (L < n || L > a.max_len) {            // lengths that cannot hold the chunk: NaN rows
-#pragma unroll
-    for (int k = 0; k < NT; ++k)
-      if (ok[k])
-        for (int d = gl; d < D; d += 4) orow[k][d] = __builtin_nanf("");
+  const int tok = t0 + col / G;               // the column's token and query head g * G + col % G
+  const bool ok = tok < n;
+  float* orow = a.out + ((size_t)(r0 + tok) * a.Hq + (size_t)g * G + col % G) * D;
+  if (L < n || L > a.max_len) {  // lengths that cannot hold the chunk: NaN rows
+    if (ok)
+      for (int d = hl; d < D; d += 2) orow[d] = __builtin_nanf("");
     return;
   }
-  int p_col[NT];                                                      // last key each column sees
-#pragma unroll
-  for (int k = 0; k < NT; ++k) p_col[k] = ok[k] ? L - n + tk[k] : -1;
+  const int p_col = ok ? L - n + tok : -1;                            // last key this column sees
   const int p_wave = t0 < n ? L - n + min(t0 + WT, n) - 1 : -1;       // last key of this wave
   const int p_first = L - n + t0;                                     // last key of the wave's first column
   const int p_wg = L - n + min(wg_t0 + kWavesPerWG * WT, n) - 1;      // last key of the workgroup
@@ -151,27 +127,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const char* kbase = static_cast<const char*>(a.k) + (size_t)g * ROW;
   const char* vbase = static_cast<const char*>(a.v) + (size_t)g * ROW;
 
-  // q^T operands: column cl of tile k is query row r0 + tk[k], head g * G + h.
-  bf16x8 q[NT][KSTEPS];
+  // q^T operands: for score product j the lane holds d = 16 j + 8 hl .. + 7
+  // of its column.
+  bf16x8 q[KS];
+  {
+    const char* qsrc = static_cast<const char*>(a.q) + ((size_t)(r0 + tok) * a.Hq + (size_t)g * G + col % G) * ROW;
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    const char* qsrc = static_cast<const char*>(a.q) + ((size_t)(r0 + tk[k]) * a.Hq + (size_t)g * G + h) * ROW;
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
+    for (int j = 0; j < KS; ++j) {
       uint4 v4 = make_uint4(0, 0, 0, 0);
-      if (ok[k]) v4 = *reinterpret_cast<const uint4*>(qsrc + 16 * (gl + 4 * j));
-      q[k][j] = __builtin_bit_cast(bf16x8, make_u32x4(v4));
+      if (ok) v4 = *reinterpret_cast<const uint4*>(qsrc + 32 * j + 16 * hl);
+      q[j] = __builtin_bit_cast(bf16x8, make_u32x4(v4));
     }
   }
-  f32x4 acc[NT][CW];
-  float m_run[NT], l_run[NT];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int dt = 0; dt < CW; ++dt) acc[k][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    m_run[k] = kNegBig;
-    l_run[k] = 0.0f;
-  }
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+  float m_run = kNegBig, l_run = 0.0f;  // l_run: this lane's half of the column's keys
 
   // Tile loads: wave w moves rows w RPW .. w RPW + RPW - 1 of the tile (K
   // and V), so each wave builds the addresses of one piece of one block;
@@ -230,127 +203,113 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       *reinterpret_cast<u32x4*>(s_v[buf] + krow * VROW + (lp + LPW * jj) * 16) = vr[jj];
     }
   };
-  // V operand of output tile dt (columns d = 16 dt + i, i < 16) by two
+  // V operand of output block db for keys 16 m .. 16 m + 15 of a step by two
   // transposing reads (ds_read_b64_tr_b16): within a group of 16 lanes, lane
-  // i receives as element j the 16-bit element i % 4 of the 8 bytes that
-  // lane 4 j + i / 4 addresses (measured lane layout on gfx950).  Lane
-  // 4 j + q of group gl addresses row 4 gl + j (16 + 4 gl + j for the second
-  // read), columns 16 dt + 4 q .. + 3, so lane (gl, cl) gets column
-  // 16 dt + cl of keys 4 gl + 0..3 and 16 + 4 gl + 0..3: the k slots of its
-  // weights.
+  // i receives as element e the 16-bit element i % 4 of the 8 bytes that
+  // lane 4 e + i / 4 addresses (measured lane layout on gfx950).  Lane l
+  // addresses row 16 m + 8 t + 4 hl + (l % 16) / 4 (read t = 0, 1), columns
+  // 32 db + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3, so it receives column
+  // 32 db + l % 32 of keys 16 m + 8 t + 4 hl + 0..3: k slot 8 hl + 4 t + e of
+  // the product is key 16 m + 8 t + 4 hl + e, the key the lane's weight
+  // 8 m + 4 t + e holds.
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  const int tr_row = 4 * gl + (cl >> 2);
-  const int tr_q = cl & 3;
-  auto v_operand = [&](const char* vtile, int dt) -> bf16x8 {
-    u32x2 h[2];
+  const int tr_off = (4 * hl + ((lane & 15) >> 2)) * VROW + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  auto v_operand = [&](const char* vtile, int db, int m) -> bf16x8 {
+    u32x2 h2[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const char* src = vtile + (half * kChunk + tr_row) * VROW + 32 * dt + 8 * tr_q;
-      h[half] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src));
+    for (int t = 0; t < 2; ++t) {
+      const char* src = vtile + tr_off + (16 * m + 8 * t) * VROW + 64 * db;
+      h2[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src));
     }
-    return __builtin_bit_cast(bf16x8, u32x4{h[0][0], h[0][1], h[1][0], h[1][1]});
+    return __builtin_bit_cast(bf16x8, u32x4{h2[0][0], h2[0][1], h2[1][0], h2[1][1]});
   };
 
-  // One 32-key step for this wave's NT tiles of 16 columns.  Lane (gl, cl)
-  // ends the score products holding keys 4 gl + r (first half) and
-  // 16 + 4 gl + r (second half), r = 0..3, of its column in each tile.  The
-  // V product contracts over 32 keys with one 16x16x32 product per output
-  // tile; its k index order is the same for both operands (k slot 8 gl + i
-  // is key 4 gl + i for i < 4, 16 + 4 gl + i - 4 after), so the lane's eight
-  // weights are its B operand as they stand.
+  // One 32-key step for this wave's 32 columns.  Lane l ends the score
+  // products holding keys 8 (r / 4) + 4 hl + r % 4, r < 16, of its column;
+  // lanes l and l ^ 32 hold the column's 32 keys between them.
   auto compute = [&](int c, int buf, int sub) {
     const int cs = c * STEP;
     const char* ktile = s_k[buf] + sub * (STEP * KROW);
     const char* vtile = s_v[buf] + sub * (STEP * VROW);
-    f32x4 sc[NT][2];
+    f32x16 sc;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
 #pragma unroll
-      for (int k = 0; k < NT; ++k) sc[k][half] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      const int r = half * kChunk + cl;
-#pragma unroll
-      for (int j = 0; j < KSTEPS; ++j) {
-        const bf16x8 kop =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + r * KROW + (gl + 4 * j) * 16));
-#pragma unroll
-        for (int k = 0; k < NT; ++k) sc[k][half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[k][j], sc[k][half], 0, 0, 0);
-      }
+    for (int j = 0; j < KS; ++j) {
+      const bf16x8 kop =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + col * KROW + 32 * j + 16 * hl));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[j], sc, 0, 0, 0);
     }
 
     // Online softmax with a lazily moved reference: the running reference
-    // m_run follows a column's maximum only when the maximum exceeds it by
+    // m_run follows the column's maximum only when the maximum exceeds it by
     // more than kLazy (base 2), so weights stay below 2^kLazy and the
-    // accumulator is rescaled rarely.  Any reference gives the same
-    // softmax; only rounding depends on it, and it depends on the data
-    // alone, so results stay deterministic.  The causal mask is applied only
-    // on steps that reach past the wave's first column's last key (columns
-    // past the chunk's end are never written, so they need no mask); one
-    // branch covers the rescale of every tile.
-    float x[NT][8], mx[NT];
+    // accumulator is rescaled rarely.  Any reference gives the same softmax;
+    // only rounding depends on it, and it depends on the data alone, so
+    // results stay deterministic.  The causal mask is applied only on steps
+    // that reach past the wave's first column's last key (columns past the
+    // chunk's end are never written, so they need no mask).
+    float x[16], mx;
     auto scores_to_exponents = [&](auto masked) {
+      const int lim = p_col - cs;
+      mx = kNegBig;
 #pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        const int lim = p_col[k] - cs;
-        mx[k] = kNegBig;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = (i < 4 ? 0 : kChunk) + 4 * gl + (i & 3);
-          const float v = sc[k][i >> 2][i & 3] * a.scale_log2;
-          x[k][i] = (!decltype(masked)::value || key <= lim) ? v : -INFINITY;
-          mx[k] = fmaxf(mx[k], x[k][i]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float v = sc[r] * a.scale_log2;
+        x[r] = (!decltype(masked)::value || key <= lim) ? v : -INFINITY;
+        mx = fmaxf(mx, x[r]);
       }
     };
     if (cs + STEP - 1 > p_first) scores_to_exponents(std::true_type{});
     else scores_to_exponents(std::false_type{});
-    bool move[NT];
-    bool any_move = false;
-#pragma unroll
-    for (int k = 0; k < NT; ++k) {
-      mx[k] = max_over_lane_groups(mx[k]);
-      move[k] = mx[k] > m_run[k] + kLazy;
-      any_move = any_move || move[k];
+    {
+      // the column's other 16 keys sit in lane l ^ 32 (v_permlane32_swap with
+      // both operands x leaves a lane its own x in one result and its xor-32
+      // partner's in the other; the maximum is exact)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    if (__any(any_move)) {  // rare: a tile whose columns keep their reference is scaled by exactly 1
+    const bool move = mx > m_run + kLazy;
+    if (__any(move)) {  // rare
+      const float mn = move ? mx : m_run;
+      const float alpha = fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
 #pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        const float mn = move[k] ? mx[k] : m_run[k];
-        const float alpha = fast_exp2(m_run[k] - mn);
-        m_run[k] = mn;
-        l_run[k] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < CW; ++dt) acc[k][dt] *= alpha;
-      }
+      for (int b = 0; b < DB; ++b) acc[b] *= alpha;
     }
-    bf16x8 phi[NT], plo[NT];
+    float pw[16];
 #pragma unroll
-    for (int k = 0; k < NT; ++k) {
-      float pw[8];
+    for (int r = 0; r < 16; ++r) pw[r] = fast_exp2(x[r] - m_run);
+    l_run += (((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]))) +
+             (((pw[8] + pw[9]) + (pw[10] + pw[11])) + ((pw[12] + pw[13]) + (pw[14] + pw[15])));
+    // P^T operands of the two 16-key products, high (truncated) and low
+    // (rounded rest) bf16 parts: product m takes the lane's weights 8 m .. 8 m + 7.
+    bf16x8 phi[2], plo[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pw[i] = fast_exp2(x[k][i] - m_run[k]);
-      l_run[k] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
-      // P^T operand, high (truncated) and low (rounded rest) bf16 parts.
+    for (int m = 0; m < 2; ++m) {
       uint32_t hb[8];
       float res[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        hb[i] = __float_as_uint(pw[i]) & 0xffff0000u;
-        res[i] = pw[i] - __uint_as_float(hb[i]);
+        hb[i] = __float_as_uint(pw[8 * m + i]) & 0xffff0000u;
+        res[i] = pw[8 * m + i] - __uint_as_float(hb[i]);
       }
-      phi[k] = __builtin_bit_cast(
+      phi[m] = __builtin_bit_cast(
           bf16x8, u32x4{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3], (hb[4] >> 16) | hb[5], (hb[6] >> 16) | hb[7]});
-      plo[k] = __builtin_bit_cast(
+      plo[m] = __builtin_bit_cast(
           bf16x8, u32x4{pack_bf16_rne(res[0], res[1]), pack_bf16_rne(res[2], res[3]), pack_bf16_rne(res[4], res[5]),
                         pack_bf16_rne(res[6], res[7])});
     }
 #pragma unroll
-    for (int dt = 0; dt < CW; ++dt) {
-      const bf16x8 vt = v_operand(vtile, dt);
+    for (int b = 0; b < DB; ++b) {
 #pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        acc[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[k], acc[k][dt], 0, 0, 0);
-        acc[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[k], acc[k][dt], 0, 0, 0);
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 vt = v_operand(vtile, b, m);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, phi[m], acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, plo[m], acc[b], 0, 0, 0);
       }
     }
   };
@@ -376,20 +335,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   bad = __syncthreads_or(bad);
 
-  // Lane (gl, cl) holds output columns 16 dt + 4 gl + r of its row; the four
-  // lane groups share the running reference, their sums add.
-  const int col0 = 4 * gl;
+  // Lane l holds output columns 32 db + 8 (r / 4) + 4 hl + r % 4 of its row;
+  // lanes l and l ^ 32 share the running reference, their sums add.
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (!ok) return;
   const float nan = __builtin_nanf("");
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    float lt = l_run[k] + __shfl_xor(l_run[k], 16);
-    lt += __shfl_xor(lt, 32);
-    if (!ok[k]) continue;
+  for (int b = 0; b < DB; ++b) {
 #pragma unroll
-    for (int dt = 0; dt < CW; ++dt) {
-      const f32x4 v4 = acc[k][dt];
-      *reinterpret_cast<float4*>(orow[k] + 16 * dt + col0) =
-          bad ? make_float4(nan, nan, nan, nan) : make_float4(v4[0] / lt, v4[1] / lt, v4[2] / lt, v4[3] / lt);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 v = make_float4(acc[b][4 * q4] / lt, acc[b][4 * q4 + 1] / lt, acc[b][4 * q4 + 2] / lt,
+                                   acc[b][4 * q4 + 3] / lt);
+      *reinterpret_cast<float4*>(orow + 32 * b + 8 * q4 + 4 * hl) = bad ? make_float4(nan, nan, nan, nan) : v;
     }
   }
 }
