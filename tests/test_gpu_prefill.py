@@ -60,6 +60,7 @@ CASES = [
     ([200, 33], [200, 10], 16, 2, 64, 16),                         # G = 8, D = 64
     ([129, 64, 5], [17, 64, 5], 16, 1, 128, 32),                   # G = 16: one token per tile
     ([70, 90, 12], [70, 0, 12], 2, 1, 64, 32),                     # G = 2, a sequence with no new rows
+    ([700, 1, 260], [300, 1, 260], 2, 2, 64, 16),                 # G = 1, D = 64: several workgroup tiles
 ]
 
 
