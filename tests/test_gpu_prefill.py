@@ -77,8 +77,9 @@ def test_prefill_matches_oracle(pk, case):
 
 @pytest.mark.parametrize("case", [0, 1, 3])
 def test_prefill_negative_scale(pk, case):
-    """A negative scale (the kernel carries its sign on q) and a scale of
-    several units, against the oracle with the same scale."""
+    """A negative scale (the running maximum then tracks the smallest raw
+    score) and a scale of several units, against the oracle with the same
+    scale."""
     lens, n_new, hq, hkv, D, B = CASES[case]
     w, q_start, q = _inputs(lens, n_new, hq, hkv, D, B, 40 + case)
     for scale in (-w.scale, float(np.float32(-0.75)), float(np.float32(2.5 * w.scale))):
