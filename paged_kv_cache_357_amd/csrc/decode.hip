@@ -374,12 +374,7 @@ void decode_balanced_kernel(DecodeParams a) {
   const long long TC = (long long)NGR * uniform(pcost[a.S]);
   auto chunk_at = [&](long long x) -> long long {
     if (x >= TC) return T;
-    int sa2 = 0, sb2 = a.S;
-    while (sb2 - sa2 > 1) {
-      const int mid = (sa2 + sb2) >> 1;
-      if ((long long)NGR * uniform(pcost[mid]) <= x) sa2 = mid;
-      else sb2 = mid;
-    }
+    const int sa2 = last_at_most(pcost, a.S, NGR, x, lane);
     const int n = uniform(pref[sa2 + 1]) - uniform(pref[sa2]);
     const long long rel = x - (long long)NGR * uniform(pcost[sa2]);
     const long long seg = n + kSegCost;
@@ -392,12 +387,7 @@ void decode_balanced_kernel(DecodeParams a) {
   const long long hi = chunk_at((long long)(worker + 1) * TC / W_eff);
 
   // Locate the segment holding chunk lo: the last s with NGR * C_s <= lo.
-  int sa = 0, sb = a.S;
-  while (sb - sa > 1) {
-    const int mid = (sa + sb) >> 1;
-    if ((long long)NGR * uniform(pref[mid]) <= lo) sa = mid;
-    else sb = mid;
-  }
+  const int sa = last_at_most(pref, a.S, NGR, lo, lane);
   struct Cursor {
     int s, g, j, n, L;  // g: head group
   };
@@ -664,7 +654,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_reduce_balanced_kernel(DecodeParams a) {
   constexpr int CPL = D / 64;  // columns per lane (1 or 2)
   // Pieces whose records are loaded together (registers: KB * G * (CPL + 2)).
-  constexpr int KB = G <= 1 ? 8 : (G <= 2 ? 4 : (G <= 4 ? 2 : 1));
+  constexpr int KB = G <= 2 ? 8 : (G <= 4 ? 4 : 2);
   const int lane = threadIdx.x & 63;
   const int seg = blockIdx.x * kWavesPerWG + uniform(threadIdx.x >> 6);  // s * Hkv + kv head
   if (seg >= a.S * a.Hkv) return;

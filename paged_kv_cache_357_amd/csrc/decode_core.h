@@ -659,6 +659,25 @@ struct MfmaCore {
 
 // ------------------------------------------------- balanced share arithmetic
 
+// Last r in [0, n) with scale * pre[r] <= x, for pre nondecreasing in LDS
+// with scale * pre[0] <= x.  Each round the 64 lanes probe evenly spaced
+// positions of the interval and a ballot keeps the piece between the last
+// probe that holds and the next one, so two rounds cover 4096 entries
+// (a one-lane binary search needs one dependent LDS read per halving).
+__device__ __forceinline__ int last_at_most(const int* pre, int n, long long scale, long long x, int lane) {
+  int ra = 0, rb = n;
+  while (rb - ra > 1) {
+    const long long span = rb - ra;
+    const int pos = ra + (int)((span * lane) >> 6);
+    const unsigned long long m = __ballot(scale * pre[pos] <= x);
+    const int last = 63 - __builtin_clzll(m | 1ull);
+    const int nb = last == 63 ? rb : ra + (int)((span * (last + 1)) >> 6);
+    ra = ra + (int)((span * last) >> 6);
+    rb = nb;
+  }
+  return uniform(ra);
+}
+
 // Wave whose share contains cost position c.
 __device__ __forceinline__ long long balanced_wave_of(long long c, long long T, long long W_eff) {
   return ((c + 1) * W_eff - 1) / T;

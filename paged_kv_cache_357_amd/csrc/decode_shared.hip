@@ -373,23 +373,8 @@ void decode_shared_kernel(DecodeParams a) {
     return;
   }
   const long long TC = (long long)NGR * uniform(T_cost);
-  // Last r in [0, R) with NGR * pre[r] <= x (pre nondecreasing, pre[0] = 0):
-  // each round the 64 lanes probe evenly spaced positions of the interval and
-  // a ballot keeps the piece between the last probe that holds and the next,
-  // so at most two rounds cover 2048 groups.
-  auto last_group_at = [&](const int* pre, long long x) {
-    int ra = 0, rb = Ru;
-    while (rb - ra > 1) {
-      const long long span = rb - ra;
-      const int pos = ra + (int)((span * lane) >> 6);
-      const unsigned long long m = __ballot((long long)NGR * pre[pos] <= x);
-      const int last = 63 - __builtin_clzll(m | 1ull);
-      const int nb = last == 63 ? rb : ra + (int)((span * (last + 1)) >> 6);
-      ra = ra + (int)((span * last) >> 6);
-      rb = nb;
-    }
-    return uniform(ra);
-  };
+  // Last group r with NGR * pre[r] <= x (pre nondecreasing, pre[0] = 0).
+  auto last_group_at = [&](const int* pre, long long x) { return last_at_most(pre, Ru, NGR, x, lane); };
   auto chunk_at = [&](long long x) -> long long {
     if (x >= TC) return T;
     const int r = last_group_at(gcost, x);
