@@ -358,7 +358,7 @@ int paged_attn_prefill(float* out, const void* q, const void* k_cache, const voi
   if (!(group == 1 || group == 2 || group == 4 || group == 8 || group == 16)) return PKV_ERR_UNSUPPORTED;
   if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
   if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
-  const int tile = pkv::kWavesPerWG * pkv::kPrefillTilesPerWave * (16 / group);  // tokens per workgroup
+  const int tile = pkv::kWavesPerWG * pkv::kPrefillColumns / group;  // tokens per workgroup
   const long long n_qt = ((long long)max_q_len + tile - 1) / tile;
   const long long units = (long long)num_seqs * kv_heads * n_qt;
   if (units > 0x7fffffffLL - 4) return PKV_ERR_UNSUPPORTED;

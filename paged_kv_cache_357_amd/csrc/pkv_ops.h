@@ -8,8 +8,8 @@
 
 namespace pkv {
 
-// Prompt pass: 16-column query tiles per wave.
-constexpr int kPrefillTilesPerWave = 2;
+// Prompt pass: query columns per wave ((token, head) pairs of 32 / G tokens).
+constexpr int kPrefillColumns = 32;
 
 // Arguments of the prompt (prefill) attention kernel.
 struct PrefillParams {

@@ -75,7 +75,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // VGPRs.
 template <int D, int B, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillParams a) {
-  static_assert(kPrefillTilesPerWave * 16 == 32, "a wave takes 32 query columns");
+  static_assert(kPrefillColumns == 32, "a wave takes the 32 columns of one 32x32 product");
   constexpr int ROW = D * 2;            // bytes of one token row of one kv head
   constexpr int LPR = ROW / 16;         // 16-byte pieces per row
   constexpr int KS = D / 16;            // score products per step (16 of d each)
