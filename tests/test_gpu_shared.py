@@ -82,6 +82,24 @@ def test_stages_equal_whole_call(pk):
     assert np.array_equal(whole.view(np.uint32), split.view(np.uint32))
 
 
+def test_over_2048_sequences_take_the_plain_path(pk):
+    """More sequences than the shared prologue holds: the same entry point runs
+    the plain kernels (fused append included), still within tolerance of the
+    oracle and with the pools bit for bit."""
+    rng = np.random.default_rng(3571)
+    w = forked("shared-2100", 700, 3, 32, rng.integers(0, 16, 2100), 4, 4, 64, 16, 3572)
+    assert w.num_seqs == 2100
+    d = to_gpu(w)
+    out = shared(pk, w, d, append=True)
+    k2, v2 = pa.oracle_append(raw_numpy(w.k_cache), raw_numpy(w.v_cache), w.block_tables, w.context_lens,
+                              raw_numpy(w.k_new), raw_numpy(w.v_new), w.block_size)
+    assert np.array_equal(raw_numpy(d.k.cpu()).view(np.uint8), k2.view(np.uint8))
+    assert np.array_equal(raw_numpy(d.v.cpu()).view(np.uint8), v2.view(np.uint8))
+    seqs = sorted(set(rng.integers(0, 2100, 96).tolist()) | {0, 2047, 2048, 2099})
+    ref = oracle_out(w, lens=w.context_lens + 1, k_cache=k2, v_cache=v2, seqs=seqs)
+    assert_parity(out, ref, w, seqs=seqs, what="2100 sequences through the shared entry point")
+
+
 def test_siblings_bitwise_and_permutation(pk):
     """Siblings with the same query rows and no private tokens get bitwise
     equal rows; relabelling the pool changes no bit; the result is
