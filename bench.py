@@ -119,6 +119,9 @@ def parse():
                          "(median of 10 per size); prints one line and exits")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the prompt pass alone (--steps flushed repetitions) and print its line")
+    ap.add_argument("--wave-timing", action="store_true",
+                    help="per-wave timing of the shared-prefix stage 1 (libpagedkv_timing.so, --steps flushed "
+                         "calls of --workload); writes profiles/wave_timing_<workload>_shared.txt")
     return ap.parse_args()
 
 
@@ -590,6 +593,85 @@ def measure_prefill(pk, torch, dev, flush, stream_ptr, reps):
             "tokens_per_s": ps["seqs"] * ps["chunk"] / (pms / 1e3)}
 
 
+def wave_timing(args):
+    """Per-wave timing of the shared-prefix stage 1 from the timing build of
+    the library: --steps flushed calls of the workload's step; per call the
+    entry and stream-start spreads, the end times, the fluid finish (every
+    wave at its measured rate with the work shared out perfectly) and the
+    per-XCD mean ends; across calls, the correlation of each worker's
+    duration with itself (after each XCD's mean is removed)."""
+    import ctypes
+    import torch
+    import paged_kv_cache_357_amd as pk
+    from workloads import make_config
+    lib = pk.load_library(os.path.join(ROOT, "paged_kv_cache_357_amd", "libpagedkv_timing.so"))
+    read = lib.pkv_wave_timing_read
+    read.restype = ctypes.c_int
+    read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    n_waves = 4096
+    buf = np.zeros((n_waves, 4), dtype=np.uint64)
+
+    def fetch():
+        if read(buf.ctypes.data, n_waves) != 0:
+            raise SystemExit("pkv_wave_timing_read failed")
+        return buf.copy()
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_config(WORKLOADS[args.workload], values=False)
+    d = on_gpu(w, dev, 5)
+    st = Step(pk, torch, d, w, "shared")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        st.run()
+    torch.cuda.synchronize()
+    fetch()
+    reps = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        st.run()
+        torch.cuda.synchronize()
+        reps.append(fetch())
+    lines = [f"# Per-wave timing of the shared-prefix stage 1 on the {args.workload} step, MI355X",
+             "# (device real-time counter at 100 MHz; times in us from the earliest wave entry of each call)", "#",
+             "#   python -c 'import __graft_entry__ as g; g.build()'      # also builds libpagedkv_timing.so",
+             f"#   python bench.py --workload {args.workload} --steps {args.steps} --wave-timing", "#",
+             "# entry/start: spread of wave entries and of stream starts (end of the prologue); end: min / mean / "
+             "max;", "# fluid: finish if every wave kept its measured rate and the work were shared out perfectly;",
+             "# tail = (max end - mean end) / max end; xcd: mean end per XCD (workgroup id mod 8).", ""]
+    durs, xcds = [], None
+    for i, r in enumerate(reps):
+        live = r[:, 2] != 0
+        t = r[live].astype(np.float64)
+        base = t[:, 0].min()
+        entry, start, end = (t[:, 0] - base) / 100.0, (t[:, 1] - base) / 100.0, (t[:, 2] - base) / 100.0
+        chunks = (r[live, 3] >> np.uint64(32)).astype(np.float64)
+        wg = (r[live, 3] & np.uint64(0xffffffff)).astype(np.int64)
+        xcd = wg % 8
+        rate = chunks / np.maximum(end - start, 1e-3)
+        fluid = start.mean() + chunks.sum() / rate.sum()
+        by_x = [round(float(end[xcd == x].mean()), 1) for x in range(8)]
+        lines.append(f"call {i}: waves {int(live.sum())}; entry spread {entry.max():.2f}; start {start.min():.2f} .. "
+                     f"{start.max():.2f}; end {end.min():.1f} / {end.mean():.1f} / {end.max():.1f}; fluid {fluid:.1f}; "
+                     f"tail {(end.max() - end.mean()) / end.max():.3f}; xcd {by_x}")
+        durs.append(end - start)
+        xcds = xcd
+    if len(durs) > 1 and all(len(x) == len(durs[0]) for x in durs):
+        D = np.stack(durs)
+        R = D.copy()
+        for x in range(8):
+            R[:, xcds == x] -= R[:, xcds == x].mean(axis=1, keepdims=True)
+        c, cr = np.corrcoef(D), np.corrcoef(R)
+        off = ~np.eye(len(durs), dtype=bool)
+        lines.append("")
+        lines.append(f"per-wave duration, correlation across calls: {c[off].min():.2f} .. {c[off].max():.2f}; "
+                     f"after removing each XCD's mean: {cr[off].min():.2f} .. {cr[off].max():.2f}")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(PROFILES, f"wave_timing_{args.workload}_shared.txt"), "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -606,6 +688,9 @@ def main():
               "sequences or kv heads with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.wave_timing:
+        wave_timing(args)
+        return
     if args.prefill_only:
         import torch
         import paged_kv_cache_357_amd as pk

@@ -2,8 +2,10 @@
 
     python -m paged_kv_cache_357_amd.build
 
-produces paged_kv_cache_357_amd/libpagedkv.so (the C-ABI library) and
-paged_kv_cache_357_amd/libpkv_probes.so (benchmark probes).
+produces paged_kv_cache_357_amd/libpagedkv.so (the C-ABI library),
+paged_kv_cache_357_amd/libpkv_probes.so (benchmark probes) and
+paged_kv_cache_357_amd/libpagedkv_timing.so (the library with per-wave timing
+of the shared-prefix stage 1, for measurement).
 """
 from __future__ import annotations
 
@@ -31,15 +33,22 @@ LIBS = {
     "libpagedkv.so": ["pagedkv_api.hip", "decode.hip", "decode_shared.hip", "prefill.hip", "append.hip",
                       "block_manager.cpp"],
     "libpkv_probes.so": ["bench_probes.hip"],
+    # The same library with per-wave timing in the shared-prefix stage 1
+    # (include/pagedkv_timing.h); only bench.py --wave-timing loads it.
+    "libpagedkv_timing.so": ["pagedkv_api.hip", "decode.hip", "decode_shared.hip:timing", "prefill.hip",
+                             "append.hip", "block_manager.cpp"],
 }
+# Sources compiled a second time with extra flags: "name:variant".
+VARIANT_FLAGS = {"timing": ["-DPKV_WAVE_TIMING"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    if src.endswith(".cpp"):
-        cmd = [HOST_CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    name, _, variant = src.partition(":")
+    obj = os.path.join(BUILD, os.path.basename(name) + (f".{variant}" if variant else "") + ".o")
+    if name.endswith(".cpp"):
+        cmd = [HOST_CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, name), "-o", obj]
     else:
-        cmd = [HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *DEVICE_FLAGS, *VARIANT_FLAGS.get(variant, []), "-c", os.path.join(CSRC, name), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -229,6 +229,15 @@ __device__ int block_excl_max(int v, int* tmp) {
 
 // ---------------------------------------------------------------- stage 1
 
+#ifdef PKV_WAVE_TIMING
+// Timing build only (libpagedkv_timing.so): per stage-1 wave, the real-time
+// counter (100 MHz) at entry, when its stream starts and when its last piece
+// is queued, and (share chunks << 32) | workgroup id.  Waves that get no
+// share leave zeros; pkv_wave_timing_read copies the table out and clears it.
+constexpr int kTimingWaves = 8192;
+__device__ unsigned long long g_wave_times[kTimingWaves][4];
+#endif
+
 template <int D, int B, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_shared_kernel(DecodeParams a) {
@@ -240,6 +249,9 @@ void decode_shared_kernel(DecodeParams a) {
   __shared__ __attribute__((aligned(16))) char s_stage[kWavesPerWG][Core::kStageBytes];
   __shared__ int s_tmp[2 * kWavesPerWG];
 
+#ifdef PKV_WAVE_TIMING
+  const unsigned long long t_entry = __builtin_amdgcn_s_memrealtime();
+#endif
   const int S = a.S;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -389,6 +401,9 @@ void decode_shared_kernel(DecodeParams a) {
   const long long lo = chunk_at((long long)worker * TC / W_eff);
   const long long hi = chunk_at((long long)(worker + 1) * TC / W_eff);
 
+#ifdef PKV_WAVE_TIMING
+  const unsigned long long t_start = __builtin_amdgcn_s_memrealtime();
+#endif
   // Cursor over the chunks of the (group, head group) segments: chunk j of a
   // segment is the prefix's chunk j for j < P / 16, then the tails of the
   // members in order.  part = -1 in the prefix, else the member index.
@@ -634,6 +649,17 @@ void decode_shared_kernel(DecodeParams a) {
     for (int k = 0; k < NB; ++k) step(buf[k], bad[k], buf[(k + NB - 1) % NB], bad[(k + NB - 1) % NB]);
   }
   flush();
+#ifdef PKV_WAVE_TIMING
+  {
+    const unsigned long long t_end = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0 && w < kTimingWaves) {
+      g_wave_times[w][0] = t_entry;
+      g_wave_times[w][1] = t_start;
+      g_wave_times[w][2] = t_end;
+      g_wave_times[w][3] = ((unsigned long long)(hi - lo) << 32) | blockIdx.x;
+    }
+  }
+#endif
   int4 rec = make_int4(-1, 0, 0, 0);
   if (split >= 0) {  // the last piece began cc's segment, which later workers continue
     const long long cbase =
@@ -808,3 +834,16 @@ hipError_t launch_shared_merge(const DecodeParams& p, int head_dim, int group, h
 }
 
 }  // namespace pkv
+
+#ifdef PKV_WAVE_TIMING
+// Declared in include/pagedkv_timing.h; exported by the timing build only.
+extern "C" __attribute__((visibility("default"))) int pkv_wave_timing_read(unsigned long long* host, int n_waves) {
+  if (!host || n_waves < 0 || n_waves > pkv::kTimingWaves) return -2;
+  const size_t bytes = (size_t)n_waves * 4 * sizeof(unsigned long long);
+  if (hipMemcpyFromSymbol(host, HIP_SYMBOL(pkv::g_wave_times), bytes, 0, hipMemcpyDeviceToHost) != hipSuccess) return -6;
+  static const unsigned long long zeros[pkv::kTimingWaves][4] = {};
+  if (hipMemcpyToSymbol(HIP_SYMBOL(pkv::g_wave_times), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice) != hipSuccess)
+    return -6;
+  return 0;
+}
+#endif

@@ -39,6 +39,23 @@ def test_only_the_abi_is_exported():
     assert funcs == _declared()
 
 
+def test_timing_build_exports_the_abi_and_its_read_out():
+    """libpagedkv_timing.so (per-wave timing of the shared-prefix stage 1) is
+    the same library plus pkv_wave_timing_read, declared in its own header;
+    the product library has no timing code."""
+    path = os.path.join(os.path.dirname(pk.LIB_PATH), "libpagedkv_timing.so")
+    if not os.path.exists(path):
+        pytest.skip("timing build not built")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pagedkv_timing.h")).read(), flags=re.S)
+    extra = re.findall(r"^\s*int\s+(\w+)\s*\(", text, flags=re.M)
+    assert extra == ["pkv_wave_timing_read"]
+    out = os.popen(f"nm -D --defined-only {path}").read().split("\n")
+    funcs = sorted(ln.split()[-1] for ln in out if " T " in ln)
+    assert funcs == sorted(_declared() + extra)
+    product = os.popen(f"nm -D --defined-only {pk.LIB_PATH}").read()
+    assert "pkv_wave_timing_read" not in product
+
+
 def test_status_strings(lib):
     assert pk.status_str(0) == "ok"
     assert pk.status_str(-5).startswith("workspace")
