@@ -588,9 +588,19 @@ def measure_prefill(pk, torch, dev, flush, stream_ptr, reps):
     pms = st["median_ms"]
     flops = prefill_flops(ps["seqs"], ps["chunk"], ps["context"], ps["q_heads"], ps["head_dim"])
     tf = flops / (pms / 1e3) / 1e12
+    # Context: the same calls back to back (no flush between them), mean per call.
+    ev = HipEvents(2, stream_ptr)
+    ev.record(0)
+    for _ in range(reps):
+        prefill()
+    ev.record(1)
+    torch.cuda.synchronize()
+    warm_ms = ev.ms(0, 1) / reps
+    ev.close()
     return {"kernel": "prefill_kernel", "shape": ps, "flops": flops, "ms": pms, "times": st, "TFLOPs": tf,
             "bound": "mfma", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tf / MFMA_BF16_PEAK_TFLOPS,
-            "tokens_per_s": ps["seqs"] * ps["chunk"] / (pms / 1e3)}
+            "tokens_per_s": ps["seqs"] * ps["chunk"] / (pms / 1e3),
+            "warm_back_to_back_ms": warm_ms, "warm_TFLOPs": flops / (warm_ms / 1e3) / 1e12}
 
 
 def wave_timing(args):
