@@ -129,6 +129,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // q^T operands: for score product j the lane holds d = 16 j + 8 hl .. + 7
   // of its column.
+  // The scores are scaled by sl2 = |scale| log2(e) >= the smallest normal
+  // float: a negative scale is moved into q as a sign flip (exact), so the
+  // column maximum can be taken over the raw scores and scaled once (rounding
+  // is monotone: the same value as the maximum of the scaled scores), each
+  // weight is exp2 of one fused multiply-add, and a masked -inf stays -inf.
+  const float sl2 = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
   bf16x8 q[KS];
   {
     const char* qsrc = static_cast<const char*>(a.q) + ((size_t)(r0 + tok) * a.Hq + (size_t)g * G + col % G) * ROW;
@@ -136,6 +142,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int j = 0; j < KS; ++j) {
       uint4 v4 = make_uint4(0, 0, 0, 0);
       if (ok) v4 = *reinterpret_cast<const uint4*>(qsrc + 32 * j + 16 * hl);
+      if (a.scale_log2 < 0.0f) v4 = make_uint4(v4.x ^ 0x80008000u, v4.y ^ 0x80008000u, v4.z ^ 0x80008000u, v4.w ^ 0x80008000u);
       q[j] = __builtin_bit_cast(bf16x8, make_u32x4(v4));
     }
   }
@@ -254,11 +261,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     float x[16], mx;
     auto scores_to_exponents = [&](auto masked) {
       const int lim = p_col - cs;
-      mx = kNegBig;
+      mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float v = sc[r] * a.scale_log2;
+        const float v = sc[r];
         x[r] = (!decltype(masked)::value || key <= lim) ? v : -INFINITY;
         mx = fmaxf(mx, x[r]);
       }
@@ -270,7 +277,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       // both operands x leaves a lane its own x in one result and its xor-32
       // partner's in the other; the maximum is exact)
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
     }
     const bool move = mx > m_run + kLazy;
     if (__any(move)) {  // rare
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     float pw[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pw[r] = fast_exp2(x[r] - m_run);
+    for (int r = 0; r < 16; ++r) pw[r] = fast_exp2(fmaf(x[r], sl2, -m_run));
     l_run += (((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]))) +
              (((pw[8] + pw[9]) + (pw[10] + pw[11])) + ((pw[12] + pw[13]) + (pw[14] + pw[15])));
     // P^T operands of the two 16-key products, high (truncated) and low
