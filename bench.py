@@ -377,7 +377,8 @@ def write_traces(args):
         cmd = f"python bench.py --prefill-only --steps {args.steps}"
         what = "prompt pass at the Llama-7B shape (4 sequences, 1024-token chunks over 2048-token contexts)"
         rerun = f"python bench.py --prefill-only --steps {args.steps} --write-traces gpurun_out/trace"
-        note = [f"# The run holds 2 warm-up calls and {args.steps} timed calls, each after a 1 GiB flush (fill kernel)."]
+        note = [f"# The run holds 2 warm-up calls, {args.steps} timed calls each after a 1 GiB flush (fill kernel), and",
+                f"# {args.steps} calls back to back."]
         out = os.path.join(PROFILES, "kernel_trace_prefill_llama7b-shape.md")
     else:
         cmd = profile_command(args)
